@@ -1,0 +1,132 @@
+/*
+ * fa.h — C ABI of libfa.so: exact tiled attention (FlashAttention) for
+ * AMD MI355X (gfx950).
+ *
+ * Sources (the three web pages on FlashAttention, cited by title + section):
+ *   [DEC] "FlashAttention, Decoded: What 'IO-Aware' Actually Means"
+ *   [HFL] "FlashAttention: A Novel Attention Algorithm with IO Awareness,
+ *          Fast and Memory-Efficient"
+ *   [ODP] "FlashAttention: Fast and Memory-Efficient Exact Attention with
+ *          IO-Awareness" (opendecode.dev paper page)
+ *
+ * What every call computes: O = softmax(Q K^T * scale + mask) V, exactly
+ * (up to floating-point rounding), without writing the N x N score matrix to
+ * device memory ([DEC "Decoding the Abstract", Sentence 4]; [ODP "The key
+ * idea"]).  The backward recomputes the score tiles from Q, K and the saved
+ * per-row log-sum-exp instead of storing them ([DEC "The Hardware Picture:
+ * Why Tiling Wins"], recomputation; [ODP "The key idea"]).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every tensor pointer is a DEVICE pointer owned by the caller.
+ *   The library allocates nothing and frees nothing.  q, k, v, o, dO, dq, dk,
+ *   dv are contiguous row-major [B][H][N][d] arrays of the element type
+ *   `dtype`, with 16-byte-aligned base addresses.  lse is a contiguous
+ *   float32 [B][H][N] array (natural logarithm).  key_len is int32 [B] in
+ *   device memory.  block_mask is uint8 [nb][nb] in device memory,
+ *   nb = ceil(N / block_size), shared by every (b, h).
+ * Sizes.  B >= 1, H >= 1, N >= 1, d in {64, 128}; B*H <= 65535*65535 and
+ *   B*H*N*d < 2^31 elements per tensor.
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls
+ *   only enqueue work on it and return without synchronising.
+ * Errors.  Arguments are validated before any HIP call is made:
+ *   FA_ERR_INVALID      a null pointer, a size out of range, a non-finite
+ *                       or non-positive scale, a workspace that is too small;
+ *   FA_ERR_UNSUPPORTED  a valid request this build does not implement
+ *                       (d not in {64, 128}, block_size != 128, fp32
+ *                       backward, fp32 block-sparse);
+ *   FA_ERR_HIP          a kernel launch failed (hipGetLastError).  Faults
+ *                       during kernel execution surface at the caller's next
+ *                       synchronisation, as for any asynchronous launch.
+ * Masks.  Combined with AND.  causal: key j visible to query i iff j <= i.
+ *   key_len (nullable): key j of batch element b visible iff j < key_len[b];
+ *   key_len[b] outside [0, N] is clamped to that range.  Rows that see no
+ *   key get O = 0, lse = -inf and contribute nothing to the gradients.
+ * Thread safety.  Every call is stateless; concurrent calls on different
+ *   outputs are safe.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID = -1,
+  FA_ERR_UNSUPPORTED = -2,
+  FA_ERR_HIP = -3
+} fa_status;
+
+/* Forward.  [ODP "The key idea"]: the queries, keys and values are split
+ * into blocks that fit on-chip, a running row maximum and running row sum
+ * are kept per query, and the partial output is rescaled as each key/value
+ * tile arrives; [HFL "FlashAttention"]: one fused kernel loads its inputs
+ * from HBM once and writes the result once.
+ *   q, k, v : inputs [B][H][N][d], dtype
+ *   o       : output [B][H][N][d], dtype (same as the inputs)
+ *   lse     : output float32 [B][H][N]: scale*max_j s_ij + ln(sum_j exp(...)),
+ *             the row statistic the backward reuses; -inf for empty rows
+ *   scale   : multiplies Q K^T (usually 1/sqrt(d))
+ *   causal  : 0 or 1
+ *   key_len : NULL (no padding mask) or int32 [B]
+ * dtype FA_F32 computes with fp32 products; FA_F16/FA_BF16 use 16-bit
+ * matrix-core products with fp32 accumulation and an fp32 softmax. */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal,
+           const int32_t* key_len, int dtype, void* stream);
+
+/* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need: 4*B*H*N
+ * (one float per query row, D_i = sum_c dO_ic O_ic).  Linear in N: the
+ * method's memory grows linearly, not quadratically, in sequence length
+ * ([ODP "Why it mattered"]).  Returns 0 for invalid sizes. */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/* Backward with recomputation ([ODP "The key idea"]; [DEC "The Hardware
+ * Picture: Why Tiling Wins"]): the probabilities are rebuilt on-chip from
+ * q, k and lse; nothing of size N x N is stored.  Three launches on
+ * `stream`: D = rowsum(dO * O); dK/dV (one workgroup per key tile);
+ * dQ (one workgroup per query tile).  Deterministic (no atomics).
+ *   o, lse  : the forward's outputs for the same inputs and mask
+ *   dO      : upstream gradient [B][H][N][d], dtype
+ *   dq,dk,dv: outputs [B][H][N][d], dtype (overwritten)
+ *   workspace / workspace_bytes: device scratch >= fa_bwd_workspace_size
+ * dtype FA_F16 or FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED). */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dO, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int causal,
+           const int32_t* key_len, void* workspace, size_t workspace_bytes,
+           int dtype, void* stream);
+
+/* Block-sparse forward ([DEC "The Passage", block-sparse extension; "Key
+ * Vocabulary", block-sparse attention: attention computed only on selected
+ * blocks of the score matrix]).  Query i sees key j iff
+ * block_mask[i / block_size][j / block_size] != 0.  Unselected blocks are
+ * skipped, not masked.  block_size must be 128.  dtype FA_F16 or FA_BF16. */
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
+                       float* lse, int B, int H, int N, int d, float scale,
+                       const uint8_t* block_mask, int block_size, int dtype,
+                       void* stream);
+
+/* Block-sparse backward: fa_bwd restricted to the selected blocks. */
+int fa_bwd_blocksparse(const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* dO,
+                       void* dq, void* dk, void* dv, int B, int H, int N,
+                       int d, float scale, const uint8_t* block_mask,
+                       int block_size, void* workspace, size_t workspace_bytes,
+                       int dtype, void* stream);
+
+/* Static description of a status code ("ok", "invalid argument", ...). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

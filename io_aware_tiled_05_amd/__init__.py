@@ -1,0 +1,162 @@
+"""MI355X-native exact tiled attention (FlashAttention) — Python binding.
+
+Thin wrappers over the C ABI of ``libfa.so`` (include/fa.h) with the same
+names.  They only marshal arguments: check shapes, dtypes and devices of
+torch tensors, allocate outputs with torch, and pass raw device pointers plus
+the current HIP stream.  Every step of the computation runs in the HIP
+kernels; there is no CPU or PyTorch fallback.
+"""
+
+from __future__ import annotations
+
+import math
+
+from ._lib import (FA_BF16, FA_ERR_HIP, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_F16,  # noqa: F401
+                   FA_F32, FA_OK, FaError, check, load)
+
+__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_blocksparse", "fa_bwd_blocksparse",
+           "fa_bwd_workspace_size", "FaError", "load"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check_qkv(*ts):
+    q = ts[0]
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    for t in ts:
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v (and o, dO) must share shape and dtype")
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _key_len(key_len, q):
+    torch = _torch()
+    if key_len is None:
+        return None
+    if key_len.dtype != torch.int32 or key_len.device != q.device or key_len.numel() != q.shape[0]:
+        raise ValueError("key_len must be an int32 tensor [B] on the same GPU")
+    return key_len.contiguous()
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fa_fwd(q, k, v, scale=None, causal=False, key_len=None, out=None, lse=None,
+           stream=None):
+    """O, lse = softmax(q k^T * scale + mask) v; see include/fa.h (fa_fwd)."""
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    kl = _key_len(key_len, q)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_qkv(q, o)
+    st = load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                       _scale(scale, d), int(bool(causal)), _ptr(kl), _dtype_code(q),
+                       _stream(stream))
+    check("fa_fwd", st)
+    return o, lse
+
+
+def fa_bwd_workspace_size(B, H, N, d):
+    return int(load().fa_bwd_workspace_size(B, H, N, d))
+
+
+def _bwd_outputs(q, dq, dk, dv, workspace):
+    torch = _torch()
+    B, H, N, d = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    need = fa_bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    return dq, dk, dv, workspace
+
+
+def fa_bwd(q, k, v, o, lse, dO, scale=None, causal=False, key_len=None, dq=None, dk=None,
+           dv=None, workspace=None, stream=None):
+    """dq, dk, dv of sum(dO * O); see include/fa.h (fa_bwd)."""
+    _check_qkv(q, k, v, o, dO)
+    B, H, N, d = q.shape
+    kl = _key_len(key_len, q)
+    dq, dk, dv, ws = _bwd_outputs(q, dq, dk, dv, workspace)
+    _check_qkv(q, dq, dk, dv)
+    st = load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+                       _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)),
+                       _ptr(kl), _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(q),
+                       _stream(stream))
+    check("fa_bwd", st)
+    return dq, dk, dv
+
+
+def _block_mask(block_mask, q):
+    torch = _torch()
+    if block_mask.dtype != torch.uint8 or block_mask.device != q.device or block_mask.dim() != 2:
+        raise ValueError("block_mask must be a uint8 [nb, nb] tensor on the same GPU")
+    return block_mask.contiguous()
+
+
+def fa_fwd_blocksparse(q, k, v, block_mask, block_size=128, scale=None, out=None, lse=None,
+                       stream=None):
+    """Block-sparse forward; see include/fa.h (fa_fwd_blocksparse)."""
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    bm = _block_mask(block_mask, q)
+    nb = (N + block_size - 1) // block_size
+    if bm.shape != (nb, nb):
+        raise ValueError(f"block_mask must be [{nb}, {nb}]")
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = load().fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                   _scale(scale, d), _ptr(bm), block_size, _dtype_code(q),
+                                   _stream(stream))
+    check("fa_fwd_blocksparse", st)
+    return o, lse
+
+
+def fa_bwd_blocksparse(q, k, v, o, lse, dO, block_mask, block_size=128, scale=None, dq=None,
+                       dk=None, dv=None, workspace=None, stream=None):
+    """Block-sparse backward; see include/fa.h (fa_bwd_blocksparse)."""
+    _check_qkv(q, k, v, o, dO)
+    B, H, N, d = q.shape
+    bm = _block_mask(block_mask, q)
+    nb = (N + block_size - 1) // block_size
+    if bm.shape != (nb, nb):
+        raise ValueError(f"block_mask must be [{nb}, {nb}]")
+    dq, dk, dv, ws = _bwd_outputs(q, dq, dk, dv, workspace)
+    st = load().fa_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d),
+                                   _ptr(bm), block_size, _ptr(ws),
+                                   ws.numel() * ws.element_size(), _dtype_code(q),
+                                   _stream(stream))
+    check("fa_bwd_blocksparse", st)
+    return dq, dk, dv

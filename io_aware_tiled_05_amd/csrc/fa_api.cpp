@@ -1,0 +1,132 @@
+// fa_api.cpp — the extern "C" entry points declared in include/fa.h.
+//
+// Every argument is validated before any HIP call; a request that passes
+// validation is forwarded to the kernel launchers, which only enqueue work
+// on the caller's stream.
+#include "fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+
+int check_sizes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID;
+  const int64_t bh = int64_t(B) * H;
+  if (bh > 65535LL * 65535LL) return FA_ERR_INVALID;
+  if (bh * N * d > kMaxElems) return FA_ERR_INVALID;
+  // grid size: one workgroup per 128 rows per head
+  if (bh * ((int64_t(N) + 127) / 128) > kMaxElems) return FA_ERR_INVALID;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_scale(float scale) {
+  return (std::isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_INVALID;
+}
+
+int check_dtype(int dtype) {
+  return (dtype == FA_F32 || dtype == FA_F16 || dtype == FA_BF16) ? FA_OK : FA_ERR_INVALID;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+               int H, int N, int d, float scale, int causal, const int32_t* key_len,
+               const uint8_t* block_mask, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  int st = check_dtype(dtype);
+  if (st == FA_OK) st = check_scale(scale);
+  if (st == FA_OK) st = check_sizes(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (block_mask && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, dtype,
+                static_cast<hipStream_t>(stream)};
+  return hip_status(fa::launch_fwd(a));
+}
+
+int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+               float scale, int causal, const int32_t* key_len, const uint8_t* block_mask,
+               void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  int st = check_dtype(dtype);
+  if (st == FA_OK) st = check_scale(scale);
+  if (st == FA_OK) st = check_sizes(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (workspace_bytes < fa_bwd_workspace_size(B, H, N, d)) return FA_ERR_INVALID;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  fa::BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
+                block_mask, static_cast<float*>(workspace), dtype,
+                static_cast<hipStream_t>(stream)};
+  return hip_status(fa::launch_bwd(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int N, int d, float scale, int causal, const int32_t* key_len, int dtype,
+           void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, nullptr, dtype,
+                    stream);
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+  return size_t(4) * size_t(B) * size_t(H) * size_t(N);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+           float scale, int causal, const int32_t* key_len, void* workspace,
+           size_t workspace_bytes, int dtype, void* stream) {
+  return bwd_common(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
+                    nullptr, workspace, workspace_bytes, dtype, stream);
+}
+
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, float scale, const uint8_t* block_mask,
+                       int block_size, int dtype, void* stream) {
+  if (!block_mask) return FA_ERR_INVALID;
+  if (block_size != 128) return block_size < 1 ? FA_ERR_INVALID : FA_ERR_UNSUPPORTED;
+  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, 0, nullptr, block_mask, dtype,
+                    stream);
+}
+
+int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dO, void* dq, void* dk, void* dv, int B,
+                       int H, int N, int d, float scale, const uint8_t* block_mask,
+                       int block_size, void* workspace, size_t workspace_bytes, int dtype,
+                       void* stream) {
+  if (!block_mask) return FA_ERR_INVALID;
+  if (block_size != 128) return block_size < 1 ? FA_ERR_INVALID : FA_ERR_UNSUPPORTED;
+  return bwd_common(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, 0, nullptr,
+                    block_mask, workspace, workspace_bytes, dtype, stream);
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// fa_device.h — gfx950 device helpers shared by the attention kernels.
+//
+// Matrix-core (MFMA) operand layouts used throughout, for
+// v_mfma_f32_16x16x32_{bf16,f16} on a 64-lane wavefront, with lane = 16*g + n
+// (n = lane & 15, g = lane >> 4):
+//   A operand (16 x 32, row-major M x K): lane holds row n, k = 8g .. 8g+7
+//   B operand (32 x 16, K x N):           lane holds col n, k = 8g .. 8g+7
+//   C/D accumulator (16 x 16):            lane holds col n, rows 4g .. 4g+3
+// The order of the 32 k values inside one instruction does not change the
+// result as long as A and B use the same order, which the kernels exploit to
+// feed an accumulator straight back in as the next operand.
+//
+// ds_read_b64_tr_b16 (LDS transpose read) on gfx950: inside each group of 16
+// lanes, lane s supplies the address of 4 consecutive 16-bit elements; lane j
+// of the group receives element (j % 4) of lanes 4i + j/4, i = 0..3.  If lane
+// s points at row r0 + s/4, columns c0 + 4(s%4) .. +3 of a row-major tile,
+// lane j therefore receives column c0 + j of rows r0 .. r0+3: a 4 x 16 block
+// read column-wise.  This gives the k-contiguous operand for contractions
+// over the row index of a row-major tile (V in P·V, dO in dV, Q in dK, K in
+// dQ) without a transposing store.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element-type traits: 16-bit storage type, MFMA operand vector, rounding.
+template <typename T> struct Elt;
+
+template <> struct Elt<__bf16> {
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ f32x4 mfma(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // round-to-nearest-even conversion of two floats into one packed dword
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    __bf16 a = (__bf16)x, b = (__bf16)y;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+};
+
+template <> struct Elt<_Float16> {
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ f32x4 mfma(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    _Float16 a = (_Float16)x, b = (_Float16)y;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ typename Elt<T>::vec8 as_vec8(u32x4 u) {
+  return __builtin_bit_cast(typename Elt<T>::vec8, u);
+}
+
+// Four floats (an accumulator quarter) -> four 16-bit values in two dwords.
+template <typename T>
+__device__ __forceinline__ u32x2 pack4(f32x4 x) {
+  u32x2 r;
+  r.x = Elt<T>::pack2(x[0], x[1]);
+  r.y = Elt<T>::pack2(x[2], x[3]);
+  return r;
+}
+
+// Eight floats (two accumulator quarters) -> one 16-bit MFMA operand.
+template <typename T>
+__device__ __forceinline__ typename Elt<T>::vec8 pack8(f32x4 lo, f32x4 hi) {
+  u32x4 r;
+  r.x = Elt<T>::pack2(lo[0], lo[1]);
+  r.y = Elt<T>::pack2(lo[2], lo[3]);
+  r.z = Elt<T>::pack2(hi[0], hi[1]);
+  r.w = Elt<T>::pack2(hi[2], hi[3]);
+  return as_vec8<T>(r);
+}
+
+// 16-byte global load (zero when !valid; the address is not touched then).
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p, bool valid) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return valid ? *reinterpret_cast<const u32x4*>(p) : z;
+}
+
+__device__ __forceinline__ u32x4 lds16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void sts16(uint16_t* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Transpose read of 4 16-bit elements (see the header comment).
+__device__ __forceinline__ u32x2 lds_tr4(const uint16_t* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Elt<T>::vec8 join8(u32x2 lo, u32x2 hi) {
+  u32x4 r = {lo.x, lo.y, hi.x, hi.y};
+  return as_vec8<T>(r);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
+}
+
+__device__ __forceinline__ float fast_log2(float x) {
+  return __builtin_amdgcn_logf(x);   // v_log_f32 (base 2)
+}
+
+// max / sum over the four 16-lane groups that share a column n
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ float group_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+__device__ __forceinline__ float pos_inf() { return __builtin_huge_valf(); }
+
+// Workgroup id -> (tile rank, head index).  Workgroups are dispatched round
+// robin over the 8 XCDs (each with its own L2); when the head count is a
+// multiple of 8 every tile of one head is placed on the same XCD so that the
+// head's K/V (or Q/dO) stream is shared through that XCD's L2.  Tile rank 0
+// is dispatched first.
+__device__ __forceinline__ void map_workgroup(int id, int ntiles, int nheads,
+                                              int* rank, int* head) {
+  if ((nheads & 7) == 0) {
+    const int xcd = id & 7, slot = id >> 3, hpx = nheads >> 3;
+    *rank = slot / hpx;
+    *head = xcd + 8 * (slot % hpx);
+  } else {
+    *rank = id / nheads;
+    *head = id % nheads;
+  }
+  (void)ntiles;
+}
+
+}  // namespace fa

@@ -1,0 +1,131 @@
+"""The C ABI library (CPU only: loading, exported symbols, argument checks).
+
+Argument validation runs before any HIP call, so invalid requests can be
+made here without a GPU; nothing in this file launches a kernel.
+"""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from io_aware_tiled_05_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libfa.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_workspace_size", "fa_fwd",
+        "fa_fwd_blocksparse", "fa_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from io_aware_tiled_05_amd import _lib
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, name
+
+
+def test_status_strings(lib):
+    assert lib.fa_status_string(0) == b"ok"
+    assert lib.fa_status_string(-1) == b"invalid argument"
+    assert lib.fa_status_string(-2) == b"unsupported configuration"
+    assert lib.fa_status_string(-3) == b"HIP launch error"
+    assert lib.fa_status_string(7) == b"unknown status"
+
+
+def test_workspace_is_linear_in_N(lib):
+    assert lib.fa_bwd_workspace_size(1, 16, 16384, 64) == 4 * 16 * 16384
+    assert lib.fa_bwd_workspace_size(2, 3, 1000, 128) == 4 * 2 * 3 * 1000
+    assert lib.fa_bwd_workspace_size(0, 1, 1, 64) == 0
+
+
+# Fake, never-dereferenced, 16-byte aligned "device" addresses: validation
+# rejects every call below before anything touches them.
+P = 0x100000
+F16, BF16, F32 = 1, 2, 0
+
+
+def fwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, scale=0.125, causal=0,
+             key_len=None, dtype=BF16)
+    a.update(kw)
+    return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                      a["d"], a["scale"], a["causal"], a["key_len"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(q=P + 8), -1),                          # misaligned
+    (dict(B=0), -1), (dict(N=0), -1), (dict(H=-1), -1),
+    (dict(d=96), -2), (dict(d=32), -2),
+    (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1), (dict(scale=0.0), -1),
+    (dict(causal=2), -1), (dict(dtype=7), -1),
+    (dict(B=1 << 16, H=1 << 16, N=1), -1),        # B*H too large
+    (dict(N=1 << 20, H=64, d=64), -1),            # tensor exceeds 2^31 elements
+])
+def test_fwd_validation(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+def bwd(lib, blocksparse=False, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, dO=P, dq=P, dk=P, dv=P, B=2, H=2, N=256, d=64,
+             scale=0.125, causal=0, key_len=None, ws=P, ws_bytes=4 * 2 * 2 * 256, dtype=BF16,
+             bm=P, bs=128)
+    a.update(kw)
+    if blocksparse:
+        return lib.fa_bwd_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"],
+                                      a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["N"],
+                                      a["d"], a["scale"], a["bm"], a["bs"], a["ws"],
+                                      a["ws_bytes"], a["dtype"], None)
+    return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"], a["dq"], a["dk"],
+                      a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                      a["key_len"], a["ws"], a["ws_bytes"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dO=None), -1), (dict(dk=None), -1), (dict(ws=None), -1),
+    (dict(ws_bytes=4 * 2 * 2 * 256 - 1), -1),     # workspace too small
+    (dict(d=80), -2), (dict(dtype=F32), -2),
+    (dict(scale=-1.0), -1), (dict(N=0), -1),
+])
+def test_bwd_validation(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bm=None), -1), (dict(bs=64), -2), (dict(bs=0), -1), (dict(dtype=F32), -2),
+    (dict(ws_bytes=0), -1),
+])
+def test_blocksparse_validation(lib, kw, status):
+    assert bwd(lib, blocksparse=True, **kw) == status
+    fkw = {k: v for k, v in kw.items() if k in ("bm", "bs", "dtype")}
+    if fkw:
+        a = dict(bm=P, bs=128, dtype=BF16)
+        a.update(fkw)
+        st = lib.fa_fwd_blocksparse(P, P, P, P, P, 1, 1, 256, 64, 0.125, a["bm"], a["bs"],
+                                    a["dtype"], None)
+        assert st == status
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from io_aware_tiled_05_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()

@@ -1,0 +1,156 @@
+"""Forward parity: HIP path (through the C ABI) vs the fp64 oracle.
+
+Tolerances (max abs error on O and lse): fp32 1e-5, fp16 1e-2, bf16 2e-2.
+Inputs are seeded N(0, 1), rounded to the dtype; both sides read the same
+rounded values.
+"""
+
+import numpy as np
+import pytest
+
+from helpers import TOL, assert_close, to_dev, to_np
+from oracle import attention_fwd, attention_rows
+from workloads import WORKLOADS, Workload, make_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import io_aware_tiled_05_amd as fa
+    fa.load()
+    return fa
+
+
+def run_fwd(fa, x, dtype, causal=False, key_len=None):
+    import torch
+    q, k, v = (to_dev(x[n], dtype) for n in ("q", "k", "v"))
+    kl = None if key_len is None else torch.from_numpy(key_len.astype(np.int32)).cuda()
+    o, lse = fa.fa_fwd(q, k, v, scale=x["scale"], causal=causal, key_len=kl)
+    torch.cuda.synchronize()
+    return to_np(o), lse.cpu().numpy().astype(np.float64)
+
+
+def edge_inputs(dtype, N, d, B=2, H=3, seed=11):
+    w = Workload("edge", B, H, N, d, dtype, seed=seed)
+    return make_inputs(w)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 7, 64, 100, 129, 300])
+@pytest.mark.parametrize("mask", ["none", "causal", "pad", "causal_pad"])
+def test_fwd_shapes_and_masks(fa, dtype, d, N, mask):
+    x = edge_inputs(dtype, N, d)
+    causal = "causal" in mask
+    key_len = None
+    if "pad" in mask:
+        key_len = np.random.default_rng(N + d).integers(1, N, size=2, endpoint=True)
+    O, lse = run_fwd(fa, x, dtype, causal, key_len)
+    O_ref, lse_ref = attention_fwd(x["q"], x["k"], x["v"], x["scale"], causal=causal,
+                                   key_len=key_len)
+    print(f"[fwd {dtype} d={d} N={N} {mask}]")
+    assert_close("O", O, O_ref, TOL[dtype])
+    assert_close("lse", lse, lse_ref, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_fwd_empty_rows(fa, dtype):
+    # key_len = 0 leaves every row of that batch element without keys
+    x = edge_inputs(dtype, 70, 64)
+    key_len = np.array([0, 33])
+    O, lse = run_fwd(fa, x, dtype, False, key_len)
+    assert np.all(O[0] == 0) and np.all(np.isneginf(lse[0]))
+    O_ref, lse_ref = attention_fwd(x["q"], x["k"], x["v"], x["scale"], key_len=key_len)
+    assert_close("O", O, O_ref, TOL[dtype])
+    assert_close("lse", lse, lse_ref, TOL[dtype])
+
+
+def test_fwd_fp32_small_workload(fa):
+    w = WORKLOADS["fp32_small"]
+    x = make_inputs(w)
+    O, lse = run_fwd(fa, x, "f32")
+    O_ref, lse_ref = attention_fwd(x["q"], x["k"], x["v"], x["scale"])
+    print("[fp32_small B1 H1 N128 d64]")
+    assert_close("O", O, O_ref, 1e-5)
+    assert_close("lse", lse, lse_ref, 1e-5)
+
+
+@pytest.mark.parametrize("name", ["bert_large", "gpt2_small"])
+def test_fwd_full_workloads(fa, name):
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    O, lse = run_fwd(fa, x, w.dtype, w.causal, x["key_len"])
+    O_ref, lse_ref = attention_fwd(x["q"], x["k"], x["v"], x["scale"], causal=w.causal,
+                                   key_len=x["key_len"])
+    print(f"[{name} full]")
+    assert_close("O", O, O_ref, TOL[w.dtype])
+    assert_close("lse", lse, lse_ref, TOL[w.dtype])
+
+
+@pytest.mark.parametrize("name", ["long_causal", "long_causal_d128"])
+def test_fwd_long_causal_sampled(fa, name):
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    O, lse = run_fwd(fa, x, w.dtype, True)
+    rows = sample_rows(w, w.H, w.N, w.sample_rows)
+    print(f"[{name} sampled {len(rows)} rows]")
+    for h in sorted({h for h, _ in rows}):
+        ii = [i for hh, i in rows if hh == h]
+        Or, lr, _ = attention_rows(x["q"], x["k"], x["v"], x["scale"], 0, h, ii, causal=True)
+        assert_close(f"O h={h}", O[0, h, ii], Or, TOL[w.dtype])
+        assert_close(f"lse h={h}", lse[0, h, ii], lr, TOL[w.dtype])
+
+
+def run_fwd_bs(fa, x, dtype, bm):
+    import torch
+    q, k, v = (to_dev(x[n], dtype) for n in ("q", "k", "v"))
+    o, lse = fa.fa_fwd_blocksparse(q, k, v, torch.from_numpy(bm).cuda(), scale=x["scale"])
+    torch.cuda.synchronize()
+    return to_np(o), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("N", [128, 300, 1000])
+def test_fwd_blocksparse_small(fa, dtype, N):
+    x = edge_inputs(dtype, N, 64)
+    nb = (N + 127) // 128
+    bm = (np.random.default_rng(N).random((nb, nb)) < 0.5).astype(np.uint8)
+    bm[0, :] = 0                      # an empty block row -> empty rows
+    O, lse = run_fwd_bs(fa, x, dtype, bm)
+    O_ref, lse_ref = attention_fwd(x["q"], x["k"], x["v"], x["scale"], block_mask=bm)
+    assert_close("O", O, O_ref, TOL[dtype])
+    assert_close("lse", lse, lse_ref, TOL[dtype])
+
+
+def test_fwd_blocksparse_all_ones_equals_dense_kernel(fa):
+    x = edge_inputs("bf16", 1000, 64)
+    bm = np.ones((8, 8), np.uint8)
+    O1, l1 = run_fwd_bs(fa, x, "bf16", bm)
+    O2, l2 = run_fwd(fa, x, "bf16")
+    assert np.array_equal(O1, O2) and np.array_equal(l1, l2)
+
+
+def test_fwd_block_sparse_workload_sampled(fa):
+    import torch
+    w = WORKLOADS["block_sparse"]
+    x = make_inputs(w)
+    bm = x["block_mask"]
+    print(f"[block_sparse N={w.N} density={bm.mean():.4f}]")
+    O, lse = run_fwd_bs(fa, x, w.dtype, bm)
+    rows = sample_rows(w, w.H, w.N, w.sample_rows)
+    for h in sorted({h for h, _ in rows}):
+        ii = [i for hh, i in rows if hh == h]
+        Or, lr, _ = attention_rows(x["q"], x["k"], x["v"], x["scale"], 0, h, ii,
+                                   block_mask=bm)
+        assert_close(f"O h={h}", O[0, h, ii], Or, TOL[w.dtype])
+        assert_close(f"lse h={h}", lse[0, h, ii], lr, TOL[w.dtype])
+    del O, lse
+    torch.cuda.empty_cache()
+
+
+def test_fwd_deterministic(fa):
+    x = edge_inputs("bf16", 1000, 64)
+    a = run_fwd(fa, x, "bf16", True)
+    b = run_fwd(fa, x, "bf16", True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
