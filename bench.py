@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Throughput of the exact tiled attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one forward (fa_fwd) plus one backward (the three stages of
+fa_bwd: D = rowsum(dO * O), dK/dV, dQ) over the whole batch, inputs already
+resident in HBM.  K steps are timed between two synchronisations with HIP
+events recorded on the stream the kernels run on (torch's current stream,
+which the binding passes to the library); events between the launches give
+each kernel's average duration inside the same timed region.
+
+Metric: attention fwd+bwd TFLOPS with the algorithmic FLOP count: 4 d flops
+per visible (query, key) pair forward (Q K^T and P V) and 10 d backward
+(the recomputed Q K^T, dO V^T, P^T dO, dS^T Q, dS K); causal pairs per head
+= N (N + 1) / 2.  The fraction is against MI355X dense bf16 MFMA peak:
+256 CU x 2.4 GHz x 4096 flop/clk/CU = 2516.6 TFLOP/s.
+
+Prints one JSON line.  The default workload is the long causal one (B=1,
+H=16, N=16384, d=64, bf16), the configuration the target is quoted on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12    # 2516.6 dense bf16/fp16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources; HBM-traffic figures are only reported while
+    the kernels still match the build they were measured on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "io_aware_tiled_05_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def pairs_of(w, N=None):
+    N = w.N if N is None else N
+    per_head = N * (N + 1) // 2 if w.causal else N * N
+    return w.B * w.H * per_head
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3
+    counter summary, or None when absent or taken on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(x, w, budget_s=10.0, prefix=8192):
+    """The fp64 oracle (forward + backward) on a bounded sample of the same
+    workload: whole heads of the causal prefix of ``prefix`` tokens (a causal
+    prefix is itself a causal attention problem), one head after another
+    until ``budget_s`` of CPU time has been spent."""
+    from threadpoolctl import threadpool_info
+    from oracle import attention_bwd, attention_fwd
+    n = min(prefix, w.N)
+    t_total, heads = 0.0, 0
+    while heads < w.H and t_total < budget_s:
+        sl = (slice(0, 1), slice(heads, heads + 1), slice(0, n))
+        q, k, v, dO = (x[name][sl] for name in ("q", "k", "v", "dO"))
+        t0 = time.perf_counter()
+        attention_fwd(q, k, v, x["scale"], causal=w.causal)
+        attention_bwd(q, k, v, dO, x["scale"], causal=w.causal)
+        t_total += time.perf_counter() - t0
+        heads += 1
+    per_head = n * (n + 1) // 2 if w.causal else n * n
+    flops = 14 * w.d * per_head * heads
+    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    return {
+        "value": round(flops / t_total / 1e12, 6),
+        "unit": "TFLOPS",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle fwd+bwd on {heads} head(s) x causal prefix of {n} tokens "
+                  f"(b=0), {t_total:.1f} s; FLOPs counted as the GPU metric (14 d per pair)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_causal")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs the per-head kernels on a single "
+              "MI355X; --gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import io_aware_tiled_05_amd as fa
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    if w.block_sparse or w.key_padding or w.dtype not in ("bf16", "f16"):
+        raise SystemExit("bench.py times the dense (optionally causal) 16-bit path")
+    fa.load()
+    dev = torch.device("cuda:0")
+    x = make_inputs(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    q, k, v, dO = (torch.from_numpy(x[n]).to(dev, tdt).contiguous() for n in ("q", "k", "v", "dO"))
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d) // 4, dtype=torch.float32, device=dev)
+    scale, causal = x["scale"], w.causal
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        for i, st in enumerate((fa.FA_BWD_STAGE_D, fa.FA_BWD_STAGE_DKDV, fa.FA_BWD_STAGE_DQ)):
+            fa.fa_bwd_stage(st, q, k, v, o, lse, dO, dq, dk, dv, ws, scale=scale, causal=causal)
+            if ev is not None:
+                ev[2 + i].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+    names = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+    kms = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+           for j, nm in enumerate(names)}
+
+    P = pairs_of(w)
+    fwd_flops, bwd_flops = 4 * d * P, 10 * d * P
+    total_tflops = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+    bwd_ms = kms["bwd_pre"] + kms["bwd_dkdv"] + kms["bwd_dq"]
+    fwd_tflops = fwd_flops / (kms["fwd"] * 1e-3) / 1e12
+    bwd_tflops = bwd_flops / (bwd_ms * 1e-3) / 1e12
+
+    # dominant kernel and its algorithmic work per launch:
+    #   fwd 4 d/pair; dK/dV 8 d/pair (S, dP, dV, dK); dQ 2 d/pair (the dQ
+    #   product; its recomputed S and dP repeat work already counted)
+    algo = {"fwd": 4 * d * P, "bwd_dkdv": 8 * d * P, "bwd_dq": 2 * d * P}
+    dom = max(algo, key=lambda nm: kms[nm])
+    achieved = algo[dom] / (kms[dom] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom)}
+
+    out = {
+        "metric": "attention fwd+bwd TFLOPS & % MFMA peak, bf16 d=64, N=1K-16K, 1 GPU",
+        "value": round(total_tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic N(0,1), seeded",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                   "scale": scale, "parallelism": "none (1 GPU)"},
+        "frac_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "bwd_tflops": round(bwd_tflops, 2),
+        "fwd_frac_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+        "bwd_frac_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+        "kernel_ms": {nm: round(v, 4) for nm, v in kms.items()},
+        "wall_s_timed": round(t_wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(x, w),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -122,6 +122,25 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v,
                        int block_size, void* workspace, size_t workspace_bytes,
                        int dtype, void* stream);
 
+/* The three launches of fa_bwd / fa_bwd_blocksparse, one at a time, for
+ * callers that schedule them separately (to time each kernel, or to place
+ * them on different streams with their own events).
+ *   stage FA_BWD_STAGE_D    : workspace[i] = D_i = sum_c dO_ic O_ic
+ *   stage FA_BWD_STAGE_DKDV : dk, dv (reads the workspace written by stage 1)
+ *   stage FA_BWD_STAGE_DQ   : dq     (reads the workspace written by stage 1)
+ * Running stages 1, 2, 3 in this order on one stream equals fa_bwd.  The
+ * arguments are those of fa_bwd; block_mask non-NULL selects the
+ * block-sparse variant (then causal must be 0, key_len NULL and block_size
+ * 128; block_size is ignored otherwise).  Pointers a stage does not touch
+ * must still be valid arguments.  An unknown stage is FA_ERR_INVALID. */
+enum { FA_BWD_STAGE_D = 1, FA_BWD_STAGE_DKDV = 2, FA_BWD_STAGE_DQ = 3 };
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v,
+                 const void* o, const float* lse, const void* dO, void* dq,
+                 void* dk, void* dv, int B, int H, int N, int d, float scale,
+                 int causal, const int32_t* key_len, const uint8_t* block_mask,
+                 int block_size, void* workspace, size_t workspace_bytes,
+                 int dtype, void* stream);
+
 /* Static description of a status code ("ok", "invalid argument", ...). */
 const char* fa_status_string(int status);
 

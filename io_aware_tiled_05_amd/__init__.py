@@ -11,10 +11,11 @@ from __future__ import annotations
 
 import math
 
-from ._lib import (FA_BF16, FA_ERR_HIP, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_F16,  # noqa: F401
+from ._lib import (FA_BF16, FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ,  # noqa: F401
+                   FA_ERR_HIP, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_F16,  # noqa: F401
                    FA_F32, FA_OK, FaError, check, load)
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_blocksparse", "fa_bwd_blocksparse",
+__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_blocksparse", "fa_bwd_blocksparse", "fa_bwd_stage",
            "fa_bwd_workspace_size", "FaError", "load"]
 
 
@@ -160,3 +161,20 @@ def fa_bwd_blocksparse(q, k, v, o, lse, dO, block_mask, block_size=128, scale=No
                                    _stream(stream))
     check("fa_bwd_blocksparse", st)
     return dq, dk, dv
+
+
+def fa_bwd_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, workspace, scale=None, causal=False,
+                 key_len=None, block_mask=None, block_size=128, stream=None):
+    """One launch of the backward (FA_BWD_STAGE_D, _DKDV or _DQ); outputs and
+    workspace are caller-allocated; see include/fa.h (fa_bwd_stage)."""
+    _check_qkv(q, k, v, o, dO, dq, dk, dv)
+    B, H, N, d = q.shape
+    kl = _key_len(key_len, q)
+    bm = None if block_mask is None else _block_mask(block_mask, q)
+    st = load().fa_bwd_stage(int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                             _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
+                             _scale(scale, d), int(bool(causal)), _ptr(kl), _ptr(bm),
+                             block_size, _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _dtype_code(q),
+                             _stream(stream))
+    check("fa_bwd_stage", st)

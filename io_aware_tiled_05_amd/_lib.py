@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
+FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ = 1, 2, 3
 
 # (name, restype, argtypes) for every function in include/fa.h
 _P, _I, _F, _SZ = C.c_void_p, C.c_int, C.c_float, C.c_size_t
@@ -24,6 +25,8 @@ SIGNATURES = {
     "fa_fwd_blocksparse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _I, _I, _P]),
     "fa_bwd_blocksparse": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P,
                                 _I, _P, _SZ, _I, _P]),
+    "fa_bwd_stage": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P,
+                          _P, _I, _P, _SZ, _I, _P]),
     "fa_status_string": (C.c_char_p, [_I]),
 }
 

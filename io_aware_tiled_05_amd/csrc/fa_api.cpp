@@ -56,7 +56,8 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
 int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                float scale, int causal, const int32_t* key_len, const uint8_t* block_mask,
-               void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+               void* workspace, size_t workspace_bytes, int dtype, void* stream,
+               int stage) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
     return FA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
@@ -72,7 +73,7 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
   fa::BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
                 block_mask, static_cast<float*>(workspace), dtype,
                 static_cast<hipStream_t>(stream)};
-  return hip_status(fa::launch_bwd(a));
+  return hip_status(fa::launch_bwd(a, stage));
 }
 
 }  // namespace
@@ -96,7 +97,21 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            float scale, int causal, const int32_t* key_len, void* workspace,
            size_t workspace_bytes, int dtype, void* stream) {
   return bwd_common(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
-                    nullptr, workspace, workspace_bytes, dtype, stream);
+                    nullptr, workspace, workspace_bytes, dtype, stream, 0);
+}
+
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
+                 int N, int d, float scale, int causal, const int32_t* key_len,
+                 const uint8_t* block_mask, int block_size, void* workspace,
+                 size_t workspace_bytes, int dtype, void* stream) {
+  if (stage < FA_BWD_STAGE_D || stage > FA_BWD_STAGE_DQ) return FA_ERR_INVALID;
+  if (block_mask) {
+    if (causal || key_len) return FA_ERR_INVALID;
+    if (block_size != 128) return block_size < 1 ? FA_ERR_INVALID : FA_ERR_UNSUPPORTED;
+  }
+  return bwd_common(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
+                    block_mask, workspace, workspace_bytes, dtype, stream, stage);
 }
 
 int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -116,7 +131,7 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* 
   if (!block_mask) return FA_ERR_INVALID;
   if (block_size != 128) return block_size < 1 ? FA_ERR_INVALID : FA_ERR_UNSUPPORTED;
   return bwd_common(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, 0, nullptr,
-                    block_mask, workspace, workspace_bytes, dtype, stream);
+                    block_mask, workspace, workspace_bytes, dtype, stream, 0);
 }
 
 const char* fa_status_string(int status) {

@@ -89,6 +89,17 @@ __device__ __forceinline__ typename Elt<T>::vec8 pack8(f32x4 lo, f32x4 hi) {
   return as_vec8<T>(r);
 }
 
+// x - round16(x): the part of x a 16-bit operand loses.  pack8 of x plus
+// pack8 of the residual carries x to about 16 significant bits through two
+// MFMAs (used where a bf16-rounded operand would eat the error budget).
+template <typename T>
+__device__ __forceinline__ f32x4 residual16(f32x4 x) {
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = x[i] - (float)(T)x[i];
+  return r;
+}
+
 // 16-byte global load (zero when !valid; the address is not touched then).
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p, bool valid) {
   u32x4 z = {0u, 0u, 0u, 0u};

@@ -44,6 +44,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
-hipError_t launch_bwd(const BwdArgs& a);
+// stage 0: all three launches; 1: D only; 2: dK/dV only; 3: dQ only
+hipError_t launch_bwd(const BwdArgs& a, int stage);
 
 }  // namespace fa

@@ -91,8 +91,24 @@ def allowed_mask(rows, n_keys, causal=False, key_len=None, block_mask=None,
         ok &= cols[None, :] < int(key_len)
     if block_mask is not None:
         bm = np.asarray(block_mask).astype(bool)
-        ok &= bm[(rows // block_size)[:, None], (cols // block_size)[None, :]]
+        # expand each selected block row to block_size columns per block
+        ok &= np.repeat(bm[rows // block_size], block_size, axis=1)[:, :n_keys]
     return ok
+
+
+def _visible(ok):
+    """Indices of the keys visible to at least one row of ``ok``.
+
+    Leaving the other keys out of a materialised chunk changes nothing:
+    their masked scores are -inf and their softmax weights exactly 0.
+    """
+    return np.nonzero(ok.any(axis=0))[0]
+
+
+def _chunk(row_chunk, block_mask, block_size):
+    # with a block mask, never mix block rows in one chunk, so that each
+    # chunk only touches the key blocks its rows select
+    return min(row_chunk, block_size) if block_mask is not None else row_chunk
 
 
 def _row_softmax(S, ok):
@@ -126,15 +142,17 @@ def attention_fwd(q, k, v, scale, causal=False, key_len=None, block_mask=None,
     Nk = k.shape[2]                   # key count (equal to N except in tests)
     O = np.zeros((B, H, N, v.shape[-1]))
     lse = np.full((B, H, N), -np.inf)
+    row_chunk = _chunk(row_chunk, block_mask, block_size)
     for b in range(B):
         L = _key_len_of(key_len, b)
         for r0 in range(0, N, row_chunk):
             rows = np.arange(r0, min(N, r0 + row_chunk))
             ok = allowed_mask(rows, Nk, causal, L, block_mask, block_size)
+            idx = _visible(ok)
             for h in range(H):
-                S = scale * (q[b, h, rows] @ k[b, h].T)
-                P, lse_r, _ = _row_softmax(S, ok)
-                O[b, h, rows] = P @ v[b, h]
+                S = scale * (q[b, h, rows] @ k[b, h, idx].T)
+                P, lse_r, _ = _row_softmax(S, ok[:, idx])
+                O[b, h, rows] = P @ v[b, h, idx]
                 lse[b, h, rows] = lse_r
     return O, lse
 
@@ -152,20 +170,22 @@ def attention_bwd(q, k, v, dO, scale, causal=False, key_len=None,
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    row_chunk = _chunk(row_chunk, block_mask, block_size)
     for b in range(B):
         L = _key_len_of(key_len, b)
         for r0 in range(0, N, row_chunk):
             rows = np.arange(r0, min(N, r0 + row_chunk))
             ok = allowed_mask(rows, Nk, causal, L, block_mask, block_size)
+            idx = _visible(ok)
             for h in range(H):
-                S = scale * (q[b, h, rows] @ k[b, h].T)
-                P, _, _ = _row_softmax(S, ok)
+                S = scale * (q[b, h, rows] @ k[b, h, idx].T)
+                P, _, _ = _row_softmax(S, ok[:, idx])
                 g = dO[b, h, rows]
-                dv[b, h] += P.T @ g
-                dP = g @ v[b, h].T
+                dv[b, h, idx] += P.T @ g
+                dP = g @ v[b, h, idx].T
                 dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-                dq[b, h, rows] = scale * (dS @ k[b, h])
-                dk[b, h] += scale * (dS.T @ q[b, h, rows])
+                dq[b, h, rows] = scale * (dS @ k[b, h, idx])
+                dk[b, h, idx] += scale * (dS.T @ q[b, h, rows])
     return dq, dk, dv
 
 
@@ -182,15 +202,16 @@ def attention_rows(q, k, v, scale, b, h, rows, dO=None, causal=False,
     rows = np.asarray(rows, dtype=np.int64)
     ok = allowed_mask(rows, N, causal, _key_len_of(key_len, b), block_mask,
                       block_size)
-    S = scale * (q[rows] @ k.T)
-    P, lse_r, _ = _row_softmax(S, ok)
-    O_r = P @ v
+    idx = _visible(ok)
+    S = scale * (q[rows] @ k[idx].T)
+    P, lse_r, _ = _row_softmax(S, ok[:, idx])
+    O_r = P @ v[idx]
     dq_r = None
     if dO is not None:
         g = _f64(dO[b, h])[rows]
-        dP = g @ v.T
+        dP = g @ v[idx].T
         dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-        dq_r = scale * (dS @ k)
+        dq_r = scale * (dS @ k[idx])
     return O_r, lse_r, dq_r
 
 
@@ -212,17 +233,23 @@ def attention_key_grads(q, k, v, dO, scale, b, h, cols, causal=False,
     L = _key_len_of(key_len, b)
     dk_c = np.zeros((cols.size, k.shape[1]))
     dv_c = np.zeros((cols.size, v.shape[1]))
+    row_chunk = _chunk(row_chunk, block_mask, block_size)
     for r0 in range(0, N, row_chunk):
         rows = np.arange(r0, min(N, r0 + row_chunk))
         sees = allowed_mask(rows, N, causal, L, block_mask, block_size)
-        if not sees[:, cols].any():
+        need = sees[:, cols].any(axis=1)      # rows that see a selected key
+        if not need.any():
             continue
-        S = scale * (q[rows] @ k.T)
-        P, _, _ = _row_softmax(S, sees)
-        dP = g[rows] @ v.T
+        rows, sees = rows[need], sees[need]
+        idx = _visible(sees)                  # keys those rows see (full rows)
+        S = scale * (q[rows] @ k[idx].T)
+        P, _, _ = _row_softmax(S, sees[:, idx])
+        dP = g[rows] @ v[idx].T
         dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-        dk_c += scale * (dS[:, cols].T @ q[rows])
-        dv_c += P[:, cols].T @ g[rows]
+        pos = np.searchsorted(idx, cols)
+        hit = (pos < idx.size) & (idx[np.minimum(pos, idx.size - 1)] == cols)
+        dk_c[hit] += scale * (dS[:, pos[hit]].T @ q[rows])
+        dv_c[hit] += P[:, pos[hit]].T @ g[rows]
     return dk_c, dv_c
 
 

@@ -30,7 +30,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_workspace_size", "fa_fwd",
+        "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd",
         "fa_fwd_blocksparse", "fa_status_string"])
 
 
@@ -129,3 +129,24 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def stage(lib, st, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, dO=P, dq=P, dk=P, dv=P, B=2, H=2, N=256, d=64,
+             scale=0.125, causal=0, key_len=None, bm=None, bs=128, ws=P, ws_bytes=4 * 2 * 2 * 256,
+             dtype=BF16)
+    a.update(kw)
+    return lib.fa_bwd_stage(st, a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"], a["dq"],
+                            a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                            a["causal"], a["key_len"], a["bm"], a["bs"], a["ws"], a["ws_bytes"],
+                            a["dtype"], None)
+
+
+@pytest.mark.parametrize("st,kw,status", [
+    (0, {}, -1), (4, {}, -1), (-1, {}, -1),
+    (1, dict(ws=None), -1), (2, dict(d=96), -2), (3, dict(dtype=F32), -2),
+    (2, dict(bm=P, causal=1), -1), (2, dict(bm=P, key_len=P), -1), (3, dict(bm=P, bs=64), -2),
+    (1, dict(ws_bytes=8), -1),
+])
+def test_bwd_stage_validation(lib, st, kw, status):
+    assert stage(lib, st, **kw) == status

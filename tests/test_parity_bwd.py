@@ -1,0 +1,154 @@
+"""Backward parity: HIP path (through the C ABI) vs the fp64 oracle.
+
+Tolerances (max abs error on dQ, dK, dV): fp16 1e-2, bf16 2e-2.  The HIP
+backward consumes the HIP forward's O and lse (its own intermediate state);
+the oracle computes everything from q, k, v, dO alone.
+"""
+
+import numpy as np
+import pytest
+
+from helpers import TOL, assert_close, to_dev, to_np
+from oracle import attention_bwd, attention_key_grads, attention_rows
+from workloads import WORKLOADS, Workload, make_inputs, sample_key_rows, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import io_aware_tiled_05_amd as fa
+    fa.load()
+    return fa
+
+
+def run_fwd_bwd(fa, x, dtype, causal=False, key_len=None, block_mask=None):
+    import torch
+    q, k, v, dO = (to_dev(x[n], dtype) for n in ("q", "k", "v", "dO"))
+    s = x["scale"]
+    if block_mask is not None:
+        bm = torch.from_numpy(block_mask).cuda()
+        o, lse = fa.fa_fwd_blocksparse(q, k, v, bm, scale=s)
+        dq, dk, dv = fa.fa_bwd_blocksparse(q, k, v, o, lse, dO, bm, scale=s)
+    else:
+        kl = None if key_len is None else torch.from_numpy(key_len.astype(np.int32)).cuda()
+        o, lse = fa.fa_fwd(q, k, v, scale=s, causal=causal, key_len=kl)
+        dq, dk, dv = fa.fa_bwd(q, k, v, o, lse, dO, scale=s, causal=causal, key_len=kl)
+    torch.cuda.synchronize()
+    return to_np(dq), to_np(dk), to_np(dv)
+
+
+def edge_inputs(dtype, N, d, B=2, H=3, seed=12):
+    return make_inputs(Workload("edge", B, H, N, d, dtype, seed=seed))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 7, 64, 100, 129, 300])
+@pytest.mark.parametrize("mask", ["none", "causal", "pad", "causal_pad"])
+def test_bwd_shapes_and_masks(fa, dtype, d, N, mask):
+    x = edge_inputs(dtype, N, d)
+    causal = "causal" in mask
+    key_len = None
+    if "pad" in mask:
+        key_len = np.random.default_rng(N + d).integers(1, N, size=2, endpoint=True)
+    dq, dk, dv = run_fwd_bwd(fa, x, dtype, causal, key_len)
+    rq, rk, rv = attention_bwd(x["q"], x["k"], x["v"], x["dO"], x["scale"], causal=causal,
+                               key_len=key_len)
+    print(f"[bwd {dtype} d={d} N={N} {mask}]")
+    assert_close("dq", dq, rq, TOL[dtype])
+    assert_close("dk", dk, rk, TOL[dtype])
+    assert_close("dv", dv, rv, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_bwd_empty_rows_and_padded_keys(fa, dtype):
+    x = edge_inputs(dtype, 300, 64)
+    key_len = np.array([0, 130])       # batch 0: every row empty
+    dq, dk, dv = run_fwd_bwd(fa, x, dtype, False, key_len)
+    assert np.all(dq[0] == 0) and np.all(dk[0] == 0) and np.all(dv[0] == 0)
+    assert np.all(dk[1, :, 130:] == 0) and np.all(dv[1, :, 130:] == 0)
+    rq, rk, rv = attention_bwd(x["q"], x["k"], x["v"], x["dO"], x["scale"], key_len=key_len)
+    assert_close("dq", dq, rq, TOL[dtype])
+    assert_close("dk", dk, rk, TOL[dtype])
+    assert_close("dv", dv, rv, TOL[dtype])
+
+
+@pytest.mark.parametrize("name", ["bert_large", "gpt2_small"])
+def test_bwd_full_workloads(fa, name):
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    dq, dk, dv = run_fwd_bwd(fa, x, w.dtype, w.causal, x["key_len"])
+    rq, rk, rv = attention_bwd(x["q"], x["k"], x["v"], x["dO"], x["scale"], causal=w.causal,
+                               key_len=x["key_len"])
+    print(f"[{name} full bwd]")
+    assert_close("dq", dq, rq, TOL[w.dtype])
+    assert_close("dk", dk, rk, TOL[w.dtype])
+    assert_close("dv", dv, rv, TOL[w.dtype])
+
+
+def check_sampled(x, w, dq, dk, dv, causal=False, block_mask=None):
+    tol = TOL[w.dtype]
+    rows = sample_rows(w, w.H, w.N, w.sample_rows)
+    for h in sorted({h for h, _ in rows}):
+        ii = [i for hh, i in rows if hh == h]
+        _, _, rq = attention_rows(x["q"], x["k"], x["v"], x["scale"], 0, h, ii, dO=x["dO"],
+                                  causal=causal, block_mask=block_mask)
+        assert_close(f"dq h={h}", dq[0, h, ii], rq, tol)
+    keys = sample_key_rows(w, w.H, w.N, w.sample_keys)
+    for h in sorted({h for h, _ in keys}):
+        jj = [j for hh, j in keys if hh == h]
+        rk, rv = attention_key_grads(x["q"], x["k"], x["v"], x["dO"], x["scale"], 0, h, jj,
+                                     causal=causal, block_mask=block_mask)
+        assert_close(f"dk h={h}", dk[0, h, jj], rk, tol)
+        assert_close(f"dv h={h}", dv[0, h, jj], rv, tol)
+
+
+@pytest.mark.parametrize("name", ["long_causal", "long_causal_d128"])
+def test_bwd_long_causal_sampled(fa, name):
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    dq, dk, dv = run_fwd_bwd(fa, x, w.dtype, True)
+    print(f"[{name} sampled bwd]")
+    check_sampled(x, w, dq, dk, dv, causal=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("N", [128, 300, 1000])
+def test_bwd_blocksparse_small(fa, dtype, N):
+    x = edge_inputs(dtype, N, 64)
+    nb = (N + 127) // 128
+    bm = (np.random.default_rng(N).random((nb, nb)) < 0.5).astype(np.uint8)
+    bm[0, :] = 0          # empty rows
+    if nb > 1:
+        bm[:, 1] = 0      # keys nobody sees
+    dq, dk, dv = run_fwd_bwd(fa, x, dtype, block_mask=bm)
+    rq, rk, rv = attention_bwd(x["q"], x["k"], x["v"], x["dO"], x["scale"], block_mask=bm)
+    assert_close("dq", dq, rq, TOL[dtype])
+    assert_close("dk", dk, rk, TOL[dtype])
+    assert_close("dv", dv, rv, TOL[dtype])
+
+
+def test_bwd_blocksparse_all_ones_equals_dense_kernel(fa):
+    x = edge_inputs("bf16", 1000, 64)
+    bm = np.ones((8, 8), np.uint8)
+    a = run_fwd_bwd(fa, x, "bf16", block_mask=bm)
+    b = run_fwd_bwd(fa, x, "bf16")
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_bwd_block_sparse_workload_sampled(fa):
+    w = WORKLOADS["block_sparse"]
+    x = make_inputs(w)
+    dq, dk, dv = run_fwd_bwd(fa, x, w.dtype, block_mask=x["block_mask"])
+    print(f"[block_sparse sampled bwd, density {x['block_mask'].mean():.4f}]")
+    check_sampled(x, w, dq, dk, dv, block_mask=x["block_mask"])
+
+
+def test_bwd_deterministic(fa):
+    x = edge_inputs("bf16", 1000, 64)
+    a = run_fwd_bwd(fa, x, "bf16", True)
+    b = run_fwd_bwd(fa, x, "bf16", True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)

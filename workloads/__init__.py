@@ -48,6 +48,8 @@ class Workload:
     sample_rows: int | None = None  # sampled query rows (None: check all)
     sample_keys: int | None = None  # sampled key rows for dK/dV
     sample_key_heads: int = 2       # heads the key-row samples are drawn from
+    sample_key_blocks: int | None = None  # if set: key rows drawn inside this
+                                          # many random 128-key blocks
 
     @property
     def scale(self) -> float:
@@ -63,7 +65,8 @@ WORKLOADS = {
     "long_causal_d128": Workload("long_causal_d128", 1, 16, 16384, 128, "bf16", causal=True,
                                  seed=4, sample_rows=256, sample_keys=64),
     "block_sparse": Workload("block_sparse", 1, 8, 65536, 64, "bf16", block_sparse=True,
-                             seed=5, sample_rows=256, sample_keys=64),
+                             seed=5, sample_rows=256, sample_keys=64, sample_key_heads=1,
+                             sample_key_blocks=8),
 }
 
 
@@ -149,7 +152,9 @@ def sample_rows(w: Workload, H: int, N: int, n: int, seed: int | None = None):
 
 def sample_key_rows(w: Workload, H: int, N: int, n: int, seed: int | None = None):
     """(h, j) key rows for dK/dV checks: ``w.sample_key_heads`` heads drawn
-    at random, n key positions spread over them, plus j = 0 and j = N-1 in
+    at random, n key positions spread over them (inside
+    ``w.sample_key_blocks`` random 128-key blocks when that is set, which
+    bounds the oracle's work under a block mask), plus j = 0 and j = N-1 in
     the first drawn head."""
     rng = np.random.Generator(np.random.PCG64(
         np.random.SeedSequence((w.seed if seed is None else seed, 77))))
@@ -158,7 +163,13 @@ def sample_key_rows(w: Workload, H: int, N: int, n: int, seed: int | None = None
     pairs = set()
     per = max(1, n // nh)
     for h in heads:
-        for j in rng.choice(N, size=min(per, N), replace=False):
+        if w.sample_key_blocks:
+            nb = (N + 127) // 128
+            blocks = rng.choice(nb, size=min(w.sample_key_blocks, nb), replace=False)
+            pool = np.concatenate([np.arange(bk * 128, min(N, bk * 128 + 128)) for bk in blocks])
+        else:
+            pool = np.arange(N)
+        for j in rng.choice(pool, size=min(per, pool.size), replace=False):
             pairs.add((h, int(j)))
     pairs |= {(heads[0], 0), (heads[0], N - 1)}
     return sorted(pairs)
