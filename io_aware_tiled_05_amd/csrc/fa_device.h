@@ -28,6 +28,10 @@ namespace fa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -44,11 +48,19 @@ template <> struct Elt<__bf16> {
   static __device__ __forceinline__ f32x4 mfma(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
   // round-to-nearest-even conversion of two floats into one packed dword
+  // (one v_cvt_pk_bf16_f32)
   static __device__ __forceinline__ uint32_t pack2(float x, float y) {
-    __bf16 a = (__bf16)x, b = (__bf16)y;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f32x2 v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  }
+  // acc + lo(p) + hi(p) (v_dot2c_f32_bf16 against 1.0, 1.0)
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
   }
 };
 
@@ -57,10 +69,16 @@ template <> struct Elt<_Float16> {
   static __device__ __forceinline__ f32x4 mfma(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
   static __device__ __forceinline__ uint32_t pack2(float x, float y) {
-    _Float16 a = (_Float16)x, b = (_Float16)y;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f32x2 v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), one, acc, false);
   }
 };
 
@@ -143,6 +161,45 @@ __device__ __forceinline__ float group_max(float x) {
 __device__ __forceinline__ float group_sum(float x) {
   x += __shfl_xor(x, 16);
   return x + __shfl_xor(x, 32);
+}
+
+// XOR swizzle of the 16-byte chunks of an LDS tile row (r = tile row,
+// CPR = 16-byte chunks per row: 8 for d = 64, 16 for d = 128).  Element
+// (r, c) of a [rows][D] tile lives at r*D + ((c/8) ^ swz(r))*8 + c%8.  The
+// permutation makes both read patterns of a tile conflict-free on the 64
+// LDS banks: the row-wise 16-byte reads of 16 consecutive rows (one chunk
+// column) and the transpose reads of 4 consecutive rows x 4 chunks.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if (CPR == 8)  // bit-reversed (r >> 1) & 7
+    return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+  return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * D + (((c >> 3) ^ swz<D / 8>(r)) << 3) + (c & 7);
+}
+
+// Copy rows [row0, row0 + ROWS) of a row-major [*][D] 16-bit matrix into a
+// swizzled LDS tile with direct global->LDS loads (no VGPR staging).  NW
+// waves share the copy; rows at or past `nrows` re-read row nrows-1 (their
+// contents are never used unmasked).  Completion is tracked by vmcnt.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void load_tile_lds(const uint16_t* g, int row0, int nrows,
+                                              uint16_t* lds, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int ITER = ROWS * CPR / (64 * NW);
+  static_assert(ITER * 64 * NW == ROWS * CPR, "tile must split evenly over the waves");
+#pragma unroll
+  for (int j = 0; j < ITER; ++j) {
+    const int slot0 = (j * NW + wave) * 64;  // wave-uniform first 16-byte slot
+    const int s = slot0 + lane;
+    const int r = s / CPR, c = (s % CPR) ^ swz<CPR>(r);
+    int row = row0 + r;
+    row = row < nrows ? row : nrows - 1;
+    __builtin_amdgcn_global_load_lds(g + (size_t)row * D + c * 8, lds + slot0 * 8, 16, 0, 0);
+  }
 }
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }

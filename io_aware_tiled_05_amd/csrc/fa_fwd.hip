@@ -10,15 +10,25 @@
 // by exp(m_old - m_new).  Q is read from HBM once, O and the row statistic
 // are written once, and no score ever leaves the chip.
 //
-// Work split (16-bit path): 256 threads = 4 waves, 128 query rows per
-// workgroup, 32 per wave (two 16-column MFMA blocks).  Key/value tiles are
-// 64 rows.  Each wave computes the TRANSPOSED score tile S^T = K Q^T
-// (keys x queries) with v_mfma_f32_16x16x32, so a lane holds 4 keys of one
-// query column: the row maximum over keys is an in-register max plus two
-// cross-lane steps, and the accumulator, rounded to 16 bits, is already laid
-// out as the k-operand of the second contraction O^T += V^T P^T (V^T is read
-// from the row-major V tile with the LDS transpose read).  Softmax runs in
-// base 2 with scale*log2(e) folded into one FMA per score.
+// Work split (16-bit path): 256 threads = 4 waves per workgroup.  A wave
+// owns QW query rows (64 at d = 64, 32 at d = 128) held in registers as the
+// B operand of the transposed score tile S^T = K Q^T, computed with
+// v_mfma_f32_32x32x16: a lane holds 16 keys of one query column, so the
+// per-query reductions are in-lane plus one exchange with lane ^ 32, and
+// the scores rounded to 16 bits are already laid out as the k-operand of
+// O^T += V^T P^T (V^T comes from the row-major V tile through the LDS
+// transpose read).  Key/value tiles of 64 rows are double buffered in LDS
+// and filled with direct global->LDS loads one tile ahead of the compute.
+//
+// Softmax runs in base 2 (scale*log2(e) folded into one FMA per score).  The
+// reference maximum m is only moved when a tile could push an
+// exponentiated score above 2^8: each lane sums its 32 probabilities of the
+// tile (v_dot2c over the packed 16-bit values, which also gives the row sum
+// l of exactly the values the P V product uses) and the wave takes the
+// rescaling path only if some partial sum exceeds 256 (or is inf/NaN, which
+// is how the first tile of every row enters it).  Between rescalings the
+// output, l and m stay consistent, so the result is the same softmax up to
+// rounding; per-tile maxima are not needed on the common path.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -39,8 +49,10 @@ struct FwdParams {
   int nblk;
 };
 
-constexpr int kBR = 128;  // query rows per workgroup (= block-sparse block)
-constexpr int kBC = 64;   // key rows per LDS tile
+constexpr int kBC = 64;              // key rows per LDS tile
+constexpr int kBR = 128;             // queries per workgroup of the fp32 kernel
+constexpr int kListMax = 1024;       // block-sparse: active blocks listed per pass
+constexpr float kRescaleAt = 256.f;  // largest probability allowed between rescalings
 
 __device__ __forceinline__ int valid_keys(const int32_t* key_len, int b, int N) {
   if (!key_len) return N;
@@ -48,18 +60,33 @@ __device__ __forceinline__ int valid_keys(const int32_t* key_len, int b, int N) 
   return kl < 0 ? 0 : (kl > N ? N : kl);
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
-  constexpr int S = D + 8;        // LDS row stride (elements): +16 B pad
-  constexpr int KS = D / 32;      // k-steps of the S contraction
-  constexpr int DB = D / 16;      // 16-row blocks of O^T
-  constexpr int CPR = D / 8;      // 16-byte chunks per row
-  typedef typename Elt<T>::vec8 vec8;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBC * S];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kBC * S];
+template <int D>
+struct FwdShape {
+  static constexpr int QW = D == 64 ? 64 : 32;  // queries per wave
+  static constexpr int NQB = QW / 32;           // 32-query MFMA blocks per wave
+  static constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
+  static constexpr int DB = D / 32;             // 32-row blocks of O^T
+  static constexpr int TILE = kBC * D;          // elements per K or V tile
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
+// NW waves per workgroup; a workgroup covers NW * QW queries.
+template <typename T, int D, int NW, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdParams p) {
+  typedef FwdShape<D> Sh;
+  constexpr int QW = Sh::QW, NQB = Sh::NQB, KS = Sh::KS, DB = Sh::DB, TILE = Sh::TILE;
+  constexpr int BR = NW * QW;
+  typedef typename Elt<T>::vec8 vec8;
+  // two K and two V tile buffers, separate arrays so that the compiler can
+  // tell the buffer being filled from the one being read
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
+  __shared__ int sList[SPARSE ? kListMax : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
   int rank, bh;
   map_workgroup(blockIdx.x, p.nqt, p.BH, &rank, &bh);
   const int qt = CAUSAL ? p.nqt - 1 - rank : rank;  // longest rows first
@@ -69,142 +96,218 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const uint16_t* K = p.k + base;
   const uint16_t* V = p.v + base;
   const int L = valid_keys(p.key_len, b, N);
-  const int q0 = qt * kBR, qw = q0 + wave * 32;
+  const int q0 = qt * BR, qw = q0 + wave * QW;
+  const float c = p.c;
 
-  // This wave's queries as B operands of S^T = K Q^T (kept in registers).
-  vec8 qf[2][KS];
+  // This wave's queries as B operands of S^T = K Q^T: lane = query column
+  // l32 of block qb, k = d values 16 ks + 8 h .. +7.
+  vec8 qf[NQB][KS];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = qw + qb * 16 + n;
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int row = qw + qb * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[qb][ks] = as_vec8<T>(ldg16(Q + (size_t)row * D + ks * 32 + g * 8, row < N));
+      qf[qb][ks] = as_vec8<T>(ldg16(Q + (size_t)row * D + ks * 16 + h * 8, row < N));
   }
 
-  float m[2] = {neg_inf(), neg_inf()};  // running max of raw scores q.k
-  float l[2] = {0.f, 0.f};              // running sum (this lane's keys)
-  f32x4 acc[DB][2];                     // O^T, unnormalised
+  float m[NQB], mc[NQB], l[NQB];  // reference max (raw score), m * c, partial row sum
+  f32x16 acc[DB][NQB];            // O^T, relative to the reference
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < NQB; ++qb) {
+    m[qb] = neg_inf();
+    mc[qb] = neg_inf();  // "no reference yet": forces the rescaling path
+    l[qb] = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  int nkt = (L + kBC - 1) / kBC;
-  if (CAUSAL) {
-    const int last = (q0 + kBR < N ? q0 + kBR : N) - 1;
-    nkt = nkt < last / kBC + 1 ? nkt : last / kBC + 1;
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[db][qb][e] = 0.f;
   }
 
-  auto tile = [&](int kt0) {
-    __syncthreads();  // every wave is done with the previous tile
+  // per-lane LDS element offsets (tile-invariant)
+  // K reads: row kb*32 + l32, chunk 2 ks + h  -> kb adds 32*D
+  int koff[KS];
 #pragma unroll
-    for (int c = tid; c < kBC * CPR; c += 256) {
-      const int r = c / CPR, col = (c % CPR) * 8, key = kt0 + r;
-      const bool ok = key < N;
-      sts16(sK + r * S + col, ldg16(K + (size_t)key * D + col, ok));
-      sts16(sV + r * S + col, ldg16(V + (size_t)key * D + col, ok));
-    }
-    __syncthreads();
-    if (qw >= N) return;                      // wave has no query rows
-    if (CAUSAL && kt0 > qw + 31) return;      // tile fully above the diagonal
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = tile_off<D>(l32, ks * 16 + h * 8);
+  // V^T transpose reads: 16-lane group g4 = lane / 16; lanes of a group
+  // address rows 16a + 4h + sub/4 (+8 for the second read), columns
+  // db*32 + 16*(g4&1) + 4*(sub%4) .. +3.  a adds 16*D.
+  const int sub = lane & 15, g4 = lane >> 4;
+  int voff[2][DB];
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      voff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec, db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
 
-    f32x4 s[4][2];
+  // one 64-key tile from LDS buffer `buf` (key rows kt0 ..)
+  auto compute = [&](const uint16_t* kt, const uint16_t* vt, int kt0) {
+    if (qw >= N) return;                        // wave has no query rows
+    if (CAUSAL && kt0 > qw + QW - 1) return;    // tile above the diagonal
+
+    // S^T for 64 keys (2 blocks of 32) x QW queries
+    f32x16 s[2][NQB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][qb][e] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const vec8 a = as_vec8<T>(lds16(sK + (kb * 16 + n) * S + ks * 32 + g * 8));
+      for (int kb = 0; kb < 2; ++kb) {
+        const vec8 a = as_vec8<T>(lds16(kt + koff[ks] + kb * 32 * D));
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = Elt<T>::mfma(a, qf[qb][ks], s[kb][qb]);
+        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = Elt<T>::mfma32(a, qf[qb][ks], s[kb][qb]);
       }
 
-    // additive -inf mask, only on tiles that cross the diagonal or the end
+    // -inf on keys past key_len / above the diagonal (boundary tiles only);
+    // accumulator element 4i+j of block kb is key kt0 + 32kb + 8i + 4h + j
     const bool need_mask = (kt0 + kBC > L) || (CAUSAL && kt0 + kBC - 1 > qw);
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kt0 + kb * 16 + g * 4 + i, query = qw + qb * 16 + n;
-            if (key >= L || (CAUSAL && key > query)) s[kb][qb][i] = neg_inf();
+          for (int e = 0; e < 16; ++e) {
+            const int key = kt0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+            const int query = qw + qb * 32 + l32;
+            if (key >= L || (CAUSAL && key > query)) s[kb][qb][e] = neg_inf();
           }
     }
 
-    // online softmax update
+    // P = exp2(c s - m c), packed to 16 bits; rs = this lane's part of the
+    // tile's row sum (of the rounded values)
+    uint32_t pk[2][NQB][8];
+    float rs[NQB];
+    auto exp_pack = [&](int qb, float msc) {
+      float r = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = s[0][qb][0];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-      mx = group_max(mx);
-      const float mn = fmaxf(m[qb], mx);
-      const float msc = (mn == neg_inf()) ? 0.f : mn * p.c;
-      const float alpha = fast_exp2(m[qb] * p.c - msc);
-      m[qb] = mn;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(fmaf(s[kb][qb][i], p.c, -msc));
-          s[kb][qb][i] = e;
-          rs += e;
+        for (int e = 0; e < 8; ++e) {
+          const float x0 = fast_exp2(fmaf(s[kb][qb][2 * e], c, -msc));
+          const float x1 = fast_exp2(fmaf(s[kb][qb][2 * e + 1], c, -msc));
+          pk[kb][qb][e] = Elt<T>::pack2(x0, x1);
+          r = Elt<T>::sum2(pk[kb][qb][e], r);
         }
-      l[qb] = l[qb] * alpha + rs;
+      rs[qb] = r;
+    };
+    bool over = false;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
+    for (int qb = 0; qb < NQB; ++qb) {
+      exp_pack(qb, mc[qb]);
+      over |= !(rs[qb] <= kRescaleAt);
     }
-
-    // O^T += V^T P^T, 32 keys per MFMA k-step
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      // move the reference to the running maximum and rescale
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      vec8 pk[2];
+      for (int qb = 0; qb < NQB; ++qb) {
+        float mx = s[0][qb][0];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) pk[qb] = pack8<T>(s[2 * kk][qb], s[2 * kk + 1][qb]);
-      const int r0 = (2 * kk) * 16 + g * 4 + (n >> 2), r1 = r0 + 16;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int col = db * 16 + (n & 3) * 4;
-        const vec8 a = join8<T>(lds_tr4(sV + r0 * S + col), lds_tr4(sV + r1 * S + col));
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m[qb], mx);
+        const float msc = mn == neg_inf() ? 0.f : mn * c;
+        const float alpha = fast_exp2(m[qb] * c - msc);  // 0 while m = -inf
+        m[qb] = mn;
+        mc[qb] = mn == neg_inf() ? neg_inf() : msc;
+        l[qb] *= alpha;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) acc[db][qb] = Elt<T>::mfma(a, pk[qb], acc[db][qb]);
+        for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
+        exp_pack(qb, msc);
       }
     }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) l[qb] += rs[qb];
+
+    // O^T += V^T P^T, 16 keys per MFMA k-step (a = 16-key chunk of the tile)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const vec8 va = join8<T>(lds_tr4(vt + voff[0][db] + a * 16 * D),
+                                 lds_tr4(vt + voff[1][db] + a * 16 * D));
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const uint32_t* pp = &pk[a >> 1][qb][(a & 1) * 4];
+          const u32x4 pb = {pp[0], pp[1], pp[2], pp[3]};
+          acc[db][qb] = Elt<T>::mfma32(va, as_vec8<T>(pb), acc[db][qb]);
+        }
+      }
+    }
+    };
+
+  // Walk `ntiles` tiles (first key of tile t = key0(t)) with the copy of
+  // tile t+1 in flight while tile t is computed.  One barrier per tile.
+  auto walk = [&](int ntiles, auto key0) {
+    if (ntiles <= 0) return;
+    load_tile_lds<D, kBC, NW>(K, key0(0), N, sK0, wave, lane);
+    load_tile_lds<D, kBC, NW>(V, key0(0), N, sV0, wave, lane);
+    auto step = [&](int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t landed
+      __syncthreads();                     // ... and every wave's; tile t-1 fully read
+      if (t + 1 < ntiles) {
+        const int nk = key0(t + 1);
+        load_tile_lds<D, kBC, NW>(K, nk, N, kn, wave, lane);
+        load_tile_lds<D, kBC, NW>(V, nk, N, vn, wave, lane);
+      }
+      compute(kc, vc, key0(t));
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, sK0, sV0, sK1, sV1);
+      if (t + 1 < ntiles) step(t + 1, sK1, sV1, sK0, sV0);
+    }
+    __syncthreads();  // LDS free for the caller
   };
 
   if (SPARSE) {
+    // Active 128-key blocks of this 128-query block row, two tiles each,
+    // gathered into LDS a window of kListMax blocks at a time.
     const uint8_t* mrow = p.block_mask + (size_t)qt * p.nblk;
-    for (int jb = 0; jb < p.nblk; ++jb) {
-      if (!mrow[jb]) continue;
-      for (int t = 2 * jb; t < 2 * jb + 2 && t < nkt; ++t) tile(t * kBC);
+    for (int w0 = 0; w0 < p.nblk; w0 += kListMax) {
+      const int wend = w0 + kListMax < p.nblk ? w0 + kListMax : p.nblk;
+      int cnt = 0;
+      for (int j0 = w0; j0 < wend; j0 += 64) {
+        const int jb = j0 + lane;
+        const bool on = jb < wend && mrow[jb] != 0;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
+        if (wave == 0 && on) sList[cnt + __builtin_popcountll(bal & ((1ull << lane) - 1))] = jb;
+        cnt += __builtin_popcountll(bal);
+      }
+      __syncthreads();
+      walk(2 * cnt, [&](int t) { return sList[t >> 1] * 128 + (t & 1) * kBC; });
     }
   } else {
-    for (int t = 0; t < nkt; ++t) tile(t * kBC);
+    int nkt = (L + kBC - 1) / kBC;
+    if (CAUSAL) {
+      const int last = (q0 + BR < N ? q0 + BR : N) - 1;
+      nkt = nkt < last / kBC + 1 ? nkt : last / kBC + 1;
+    }
+    walk(nkt, [](int t) { return t * kBC; });
   }
 
-  // epilogue: O = O^T / l, lse = scale*m + ln(l)
+  // epilogue: O = O^T / l, lse = (m c + log2 l) ln 2
   uint16_t* O = p.o + base;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float lt = group_sum(l[qb]);
-    const int query = qw + qb * 16 + n;
+  for (int qb = 0; qb < NQB; ++qb) {
+    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    const int query = qw + qb * 32 + l32;
     if (query < N) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<u32x2*>(O + (size_t)query * D + db * 16 + g * 4) =
-            pack4<T>(acc[db][qb] * inv);
-      if (g == 0)
-        p.lse[(size_t)bh * N + query] =
-            lt > 0.f ? (m[qb] * p.c + fast_log2(lt)) * kLn2 : neg_inf();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 o4 = {acc[db][qb][4 * i] * inv, acc[db][qb][4 * i + 1] * inv,
+                            acc[db][qb][4 * i + 2] * inv, acc[db][qb][4 * i + 3] * inv};
+          *reinterpret_cast<u32x2*>(O + (size_t)query * D + db * 32 + 8 * i + 4 * h) = pack4<T>(o4);
+        }
+      if (h == 0)
+        p.lse[(size_t)bh * N + query] = lt > 0.f ? (mc[qb] + fast_log2(lt)) * kLn2 : neg_inf();
     }
   }
 }
@@ -356,6 +459,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParamsF32 p) {
 
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 hipError_t run_fwd(const FwdArgs& a) {
+  // block-sparse workgroups cover exactly one 128-query mask row
+  constexpr int QW = FwdShape<D>::QW;
+  constexpr int NW = SPARSE ? 128 / QW : 4;
+  constexpr int BR = NW * QW;
   FwdParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -365,13 +472,13 @@ hipError_t run_fwd(const FwdArgs& a) {
   p.H = a.H;
   p.N = a.N;
   p.BH = a.B * a.H;
-  p.nqt = (a.N + kBR - 1) / kBR;
+  p.nqt = (a.N + BR - 1) / BR;
   p.c = a.scale * kLog2e;
   p.key_len = a.key_len;
   p.block_mask = a.block_mask;
   p.nblk = (a.N + 127) / 128;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, SPARSE>), dim3(p.nqt * p.BH), dim3(256), 0,
-                     a.stream, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, NW, CAUSAL, SPARSE>), dim3(p.nqt * p.BH), dim3(64 * NW),
+                     0, a.stream, p);
   return hipGetLastError();
 }
 
