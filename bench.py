@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, --steps "
+                         "times (the known-size kernel that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the per-head kernels on a single "
@@ -116,6 +119,16 @@ def main():
 
     import io_aware_tiled_05_amd as fa
     from workloads import WORKLOADS, make_inputs
+
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "steps": args.steps}))
+        return
 
     w = WORKLOADS[args.workload]
     if w.block_sparse or w.key_padding or w.dtype not in ("bf16", "f16"):

@@ -181,26 +181,49 @@ __device__ __forceinline__ int tile_off(int r, int c) {
   return r * D + (((c >> 3) ^ swz<D / 8>(r)) << 3) + (c & 7);
 }
 
-// Copy rows [row0, row0 + ROWS) of a row-major [*][D] 16-bit matrix into a
-// swizzled LDS tile with direct global->LDS loads (no VGPR staging).  NW
-// waves share the copy; rows at or past `nrows` re-read row nrows-1 (their
-// contents are never used unmasked).  Completion is tracked by vmcnt.
+// Copies rows [row0, row0 + ROWS) of a row-major [*][D] 16-bit matrix into
+// a swizzled LDS tile with direct global->LDS loads (no VGPR staging).  NW
+// waves share the copy: 16-byte slot s of the tile (slot = 64 * instruction
+// + lane) receives row s / CPR, chunk (s % CPR) ^ swz(row).  The per-lane
+// element offsets are tile-invariant and computed once; a copy is then one
+// load per instruction from a wave-uniform base.  Rows at or past `nrows`
+// re-read row nrows-1 (their contents are never used unmasked).
+// Completion is tracked by vmcnt.
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void load_tile_lds(const uint16_t* g, int row0, int nrows,
-                                              uint16_t* lds, int wave, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int ITER = ROWS * CPR / (64 * NW);
+struct TileCopy {
+  static constexpr int CPR = D / 8;
+  static constexpr int ITER = ROWS * CPR / (64 * NW);
   static_assert(ITER * 64 * NW == ROWS * CPR, "tile must split evenly over the waves");
+  uint32_t off[ITER];  // element offset of this lane's chunk within the tile's rows
+  int wave;
+
+  __device__ __forceinline__ TileCopy(int wave_, int lane) : wave(wave_) {
 #pragma unroll
-  for (int j = 0; j < ITER; ++j) {
-    const int slot0 = (j * NW + wave) * 64;  // wave-uniform first 16-byte slot
-    const int s = slot0 + lane;
-    const int r = s / CPR, c = (s % CPR) ^ swz<CPR>(r);
-    int row = row0 + r;
-    row = row < nrows ? row : nrows - 1;
-    __builtin_amdgcn_global_load_lds(g + (size_t)row * D + c * 8, lds + slot0 * 8, 16, 0, 0);
+    for (int j = 0; j < ITER; ++j) {
+      const int s = (j * NW + wave) * 64 + lane;
+      const int r = s / CPR, c = (s % CPR) ^ swz<CPR>(r);
+      off[j] = (uint32_t)(r * D + c * 8);
+    }
   }
-}
+
+  __device__ __forceinline__ void operator()(const uint16_t* g, int row0, int nrows,
+                                             uint16_t* lds) const {
+    const uint16_t* base = g + (size_t)row0 * D;
+    if (row0 + ROWS <= nrows) {
+#pragma unroll
+      for (int j = 0; j < ITER; ++j)
+        __builtin_amdgcn_global_load_lds(base + off[j], lds + (j * NW + wave) * 512, 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < ITER; ++j) {
+        const int r = (int)(off[j] / D);
+        const int last = nrows - 1 - row0;  // last valid row, relative to row0
+        const uint32_t o = r <= last ? off[j] : off[j] - (uint32_t)((r - last) * D);
+        __builtin_amdgcn_global_load_lds(base + o, lds + (j * NW + wave) * 512, 16, 0, 0);
+      }
+    }
+  }
+};
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 __device__ __forceinline__ float pos_inf() { return __builtin_huge_valf(); }

@@ -34,7 +34,7 @@
 
 namespace fa {
 
-namespace {
+namespace fwd {
 
 struct FwdParams {
   const uint16_t* q;
@@ -49,6 +49,14 @@ struct FwdParams {
   int nblk;
 };
 
+// Compile-time tuning knobs (defaults are the measured best).
+#ifndef FA_FWD_QW64
+#define FA_FWD_QW64 64  // queries per wave at d = 64 (32 or 64)
+#endif
+#ifndef FA_FWD_WAVES_PER_SIMD
+#define FA_FWD_WAVES_PER_SIMD 2
+#endif
+
 constexpr int kBC = 64;              // key rows per LDS tile
 constexpr int kBR = 128;             // queries per workgroup of the fp32 kernel
 constexpr int kListMax = 1024;       // block-sparse: active blocks listed per pass
@@ -62,7 +70,7 @@ __device__ __forceinline__ int valid_keys(const int32_t* key_len, int b, int N) 
 
 template <int D>
 struct FwdShape {
-  static constexpr int QW = D == 64 ? 64 : 32;  // queries per wave
+  static constexpr int QW = D == 64 ? FA_FWD_QW64 : 32;  // queries per wave
   static constexpr int NQB = QW / 32;           // 32-query MFMA blocks per wave
   static constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;             // 32-row blocks of O^T
@@ -71,7 +79,7 @@ struct FwdShape {
 
 // NW waves per workgroup; a workgroup covers NW * QW queries.
 template <typename T, int D, int NW, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(FwdParams p) {
   typedef FwdShape<D> Sh;
   constexpr int QW = Sh::QW, NQB = Sh::NQB, KS = Sh::KS, DB = Sh::DB, TILE = Sh::TILE;
   constexpr int BR = NW * QW;
@@ -182,7 +190,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdParams p) {
     uint32_t pk[2][NQB][8];
     float rs[NQB];
     auto exp_pack = [&](int qb, float msc) {
-      float r = 0.f;
+      float r[4] = {0.f, 0.f, 0.f, 0.f};  // four independent sum chains
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -190,9 +198,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdParams p) {
           const float x0 = fast_exp2(fmaf(s[kb][qb][2 * e], c, -msc));
           const float x1 = fast_exp2(fmaf(s[kb][qb][2 * e + 1], c, -msc));
           pk[kb][qb][e] = Elt<T>::pack2(x0, x1);
-          r = Elt<T>::sum2(pk[kb][qb][e], r);
+          r[e & 3] = Elt<T>::sum2(pk[kb][qb][e], r[e & 3]);
         }
-      rs[qb] = r;
+      rs[qb] = (r[0] + r[1]) + (r[2] + r[3]);
     };
     bool over = false;
 #pragma unroll
@@ -239,21 +247,23 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdParams p) {
         }
       }
     }
-    };
+  };
+
+  const TileCopy<D, kBC, NW> copy(wave, lane);
 
   // Walk `ntiles` tiles (first key of tile t = key0(t)) with the copy of
   // tile t+1 in flight while tile t is computed.  One barrier per tile.
   auto walk = [&](int ntiles, auto key0) {
     if (ntiles <= 0) return;
-    load_tile_lds<D, kBC, NW>(K, key0(0), N, sK0, wave, lane);
-    load_tile_lds<D, kBC, NW>(V, key0(0), N, sV0, wave, lane);
+    copy(K, key0(0), N, sK0);
+    copy(V, key0(0), N, sV0);
     auto step = [&](int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t landed
       __syncthreads();                     // ... and every wave's; tile t-1 fully read
       if (t + 1 < ntiles) {
         const int nk = key0(t + 1);
-        load_tile_lds<D, kBC, NW>(K, nk, N, kn, wave, lane);
-        load_tile_lds<D, kBC, NW>(V, nk, N, vn, wave, lane);
+        copy(K, nk, N, kn);
+        copy(V, nk, N, vn);
       }
       compute(kc, vc, key0(t));
     };
@@ -457,6 +467,24 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParamsF32 p) {
   }
 }
 
+// Explicit instantiations of every kernel the launchers below can select.
+// (Without them the host pass of this compiler leaves some kernel-template
+// launch stubs undefined.)
+#define FA_FWD_INSTANTIATE(T, D)                                                              \
+  template __global__ void fwd_kernel<T, D, 128 / FwdShape<D>::QW, false, true>(FwdParams);  \
+  template __global__ void fwd_kernel<T, D, 4, true, false>(FwdParams);                      \
+  template __global__ void fwd_kernel<T, D, 4, false, false>(FwdParams);
+
+FA_FWD_INSTANTIATE(__bf16, 64)
+FA_FWD_INSTANTIATE(__bf16, 128)
+FA_FWD_INSTANTIATE(_Float16, 64)
+FA_FWD_INSTANTIATE(_Float16, 128)
+#undef FA_FWD_INSTANTIATE
+template __global__ void fwd_f32_kernel<64, true>(FwdParamsF32);
+template __global__ void fwd_f32_kernel<64, false>(FwdParamsF32);
+template __global__ void fwd_f32_kernel<128, true>(FwdParamsF32);
+template __global__ void fwd_f32_kernel<128, false>(FwdParamsF32);
+
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 hipError_t run_fwd(const FwdArgs& a) {
   // block-sparse workgroups cover exactly one 128-query mask row
@@ -506,7 +534,9 @@ hipError_t dispatch_mask(const FwdArgs& a) {
   return a.causal ? run_fwd<T, D, true, false>(a) : run_fwd<T, D, false, false>(a);
 }
 
-}  // namespace
+}  // namespace fwd
+
+using namespace fwd;
 
 hipError_t launch_fwd(const FwdArgs& a) {
   if (a.dtype == 0) {  // FA_F32

@@ -41,6 +41,22 @@ def test_library_exports_every_declared_symbol(lib):
         assert name in _lib.SIGNATURES, name
 
 
+def test_library_has_no_undefined_kernel_stubs(lib):
+    # every kernel the launchers can select must have its host launch stub
+    # in the library; a missing one only fails when the library is opened on
+    # a machine with a GPU
+    import shutil
+    import subprocess
+    from io_aware_tiled_05_amd import _lib
+    nm = shutil.which("nm") or shutil.which("llvm-nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    stubs = [line for line in out.splitlines() if "__device_stub__" in line]
+    assert stubs == [], stubs
+
+
 def test_status_strings(lib):
     assert lib.fa_status_string(0) == b"ok"
     assert lib.fa_status_string(-1) == b"invalid argument"
