@@ -82,8 +82,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal,
            const int32_t* key_len, int dtype, void* stream);
 
-/* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need: 4*B*H*N
- * (one float per query row, D_i = sum_c dO_ic O_ic).  Linear in N: the
+/* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need: 8*B*H*N
+ * (two floats per query row: D_i = sum_c dO_ic O_ic and the base-2 softmax
+ * shift lse_i * log2(e), +inf for rows without keys).  Linear in N: the
  * method's memory grows linearly, not quadratically, in sequence length
  * ([ODP "Why it mattered"]).  Returns 0 for invalid sizes. */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
@@ -125,7 +126,8 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v,
 /* The three launches of fa_bwd / fa_bwd_blocksparse, one at a time, for
  * callers that schedule them separately (to time each kernel, or to place
  * them on different streams with their own events).
- *   stage FA_BWD_STAGE_D    : workspace[i] = D_i = sum_c dO_ic O_ic
+ *   stage FA_BWD_STAGE_D    : workspace[i] = D_i = sum_c dO_ic O_ic and
+ *                             workspace[B*H*N + i] = lse_i * log2(e)
  *   stage FA_BWD_STAGE_DKDV : dk, dv (reads the workspace written by stage 1)
  *   stage FA_BWD_STAGE_DQ   : dq     (reads the workspace written by stage 1)
  * Running stages 1, 2, 3 in this order on one stream equals fa_bwd.  The

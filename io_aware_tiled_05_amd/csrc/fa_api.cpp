@@ -89,7 +89,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
-  return size_t(4) * size_t(B) * size_t(H) * size_t(N);
+  return size_t(8) * size_t(B) * size_t(H) * size_t(N);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -14,26 +14,32 @@
 // dK = scale dS^T Q.
 //
 // Three launches, no atomics (deterministic):
-//   bwd_pre   D for every query row (bandwidth-bound, one pass over O, dO);
-//   bwd_dkdv  one workgroup per 128 keys (32 per wave), query tiles of 64
-//             rows streamed through LDS: S = Q K^T and dP = dO V^T come out
-//             with the key in the lane's column, so bf16(P) and bf16(dS) are
-//             directly the k-operands of dV^T += dO^T P and dK^T += Q^T dS
-//             (dO^T and Q^T via the LDS transpose read);
-//   bwd_dq    one workgroup per 128 queries (32 per wave), key tiles of 64
-//             rows streamed through LDS: S^T = K Q^T and dP^T = V dO^T keep
-//             the query in the lane's column, and dQ^T += K^T dS^T.
+//   bwd_pre   per query row: D and the base-2 softmax shift lse*log2(e)
+//             (+inf for rows without keys), into the workspace;
+//   bwd_dkdv  one workgroup per 128 keys (32 per wave); query tiles of 64
+//             rows (Q, dO, shift, D) are double buffered in LDS.  With
+//             v_mfma_f32_32x32x16, S = Q K^T and dP = dO V^T come out with
+//             the key in the lane's column, so P and dS rounded to 16 bits
+//             are directly the k-operands of dV^T += dO^T P and
+//             dK^T += Q^T dS (dO^T and Q^T via the LDS transpose read);
+//   bwd_dq    one workgroup per 128 queries (32 per wave); key tiles of 64
+//             rows (K, V) double buffered in LDS: S^T = K Q^T and
+//             dP^T = V dO^T keep the query in the lane's column, and
+//             dQ^T += K^T dS^T.
+// LDS tiles are XOR-swizzled (conflict-free row and transpose reads) and
+// filled by direct global->LDS copies one tile ahead of the compute.
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 
-namespace {
+namespace bwd {
 
-constexpr int kBKV = 128;  // keys per dK/dV workgroup (= block-sparse block)
-constexpr int kBQ = 64;    // query rows per LDS tile in the dK/dV kernel
-constexpr int kBR = 128;   // queries per dQ workgroup (= block-sparse block)
-constexpr int kBC = 64;    // key rows per LDS tile in the dQ kernel
+constexpr int kBKV = 128;      // keys per dK/dV workgroup (= block-sparse block)
+constexpr int kBQ = 64;        // query rows per LDS tile in the dK/dV kernel
+constexpr int kBR = 128;       // queries per dQ workgroup (= block-sparse block)
+constexpr int kBC = 64;        // key rows per LDS tile in the dQ kernel
+constexpr int kListMax = 1024; // block-sparse: active blocks listed per pass
 
 template <typename T> constexpr bool kIsBf16 = false;
 template <> constexpr bool kIsBf16<__bf16> = true;
@@ -53,11 +59,13 @@ __device__ __forceinline__ int valid_keys(const int32_t* key_len, int b, int N) 
 }
 
 // ---------------------------------------------------------------------------
-// D_i = sum_c dO_ic O_ic
+// Per row: D_i = sum_c dO_ic O_ic and shift_i = lse_i * log2(e) (+inf when
+// the row saw no key, so that exp2(c s - shift) = 0 there).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const uint16_t* dO,
-                                                      float* Dbuf, int64_t rows) {
+                                                      const float* lse, float* Dbuf,
+                                                      float* shift, int64_t rows) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements (16 B) each
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid / TPR;
@@ -74,7 +82,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (row < rows && c == 0) Dbuf[row] = s;
+  if (row < rows && c == 0) {
+    Dbuf[row] = s;
+    const float l = lse[row];
+    shift[row] = l == neg_inf() ? pos_inf() : l * kLog2e;
+  }
 }
 
 struct BwdParams {
@@ -82,7 +94,7 @@ struct BwdParams {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dO;
-  const float* lse;
+  const float* shift;  // lse * log2(e), +inf for rows without keys
   const float* Dbuf;
   uint16_t* dq;
   uint16_t* dk;
@@ -95,26 +107,77 @@ struct BwdParams {
   int nblk;
 };
 
-// lse (natural log) -> the base-2 shift used in exp2(c*s - shift); rows
-// without keys (lse = -inf) get +inf so that their probabilities are 0.
-__device__ __forceinline__ float lse_shift(float lse) {
-  return lse == neg_inf() ? pos_inf() : lse * kLog2e;
+// B operand (P or dS, 16 keys or queries of chunk a) from a 32x32
+// accumulator: chunk a covers accumulator elements 8(a%2) .. 8(a%2)+7 of
+// block a/2, i.e. rows 16a + 4h + 0..3 and 16a + 8 + 4h + 0..3.
+template <typename T>
+__device__ __forceinline__ typename Elt<T>::vec8 pack_chunk(const f32x16& x, int half) {
+  u32x4 r;
+  r.x = Elt<T>::pack2(x[8 * half + 0], x[8 * half + 1]);
+  r.y = Elt<T>::pack2(x[8 * half + 2], x[8 * half + 3]);
+  r.z = Elt<T>::pack2(x[8 * half + 4], x[8 * half + 5]);
+  r.w = Elt<T>::pack2(x[8 * half + 6], x[8 * half + 7]);
+  return as_vec8<T>(r);
+}
+
+// the part of the same eight values a 16-bit rounding loses
+template <typename T>
+__device__ __forceinline__ typename Elt<T>::vec8 pack_chunk_lo(const f32x16& x, int half) {
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = x[8 * half + i] - (float)(T)x[8 * half + i];
+  u32x4 u;
+  u.x = Elt<T>::pack2(r[0], r[1]);
+  u.y = Elt<T>::pack2(r[2], r[3]);
+  u.z = Elt<T>::pack2(r[4], r[5]);
+  u.w = Elt<T>::pack2(r[6], r[7]);
+  return as_vec8<T>(u);
+}
+
+// Copy of 64 consecutive fp32 values (one per lane) into LDS, by wave 0.
+__device__ __forceinline__ void copy_row_stat(const float* g, int row0, int nrows, float* lds,
+                                              int lane) {
+  int row = row0 + lane;
+  row = row < nrows ? row : nrows - 1;
+  __builtin_amdgcn_global_load_lds(g + row, lds, 4, 0, 0);
+}
+
+// Active 128-blocks of one mask row (stride 1) or column (stride nblk),
+// window [w0, wend), gathered into lst by wave 0; every wave gets the count.
+__device__ __forceinline__ int list_blocks(const uint8_t* m, int stride, int w0, int wend,
+                                           int* lst, int wave, int lane) {
+  int cnt = 0;
+  for (int j0 = w0; j0 < wend; j0 += 64) {
+    const int j = j0 + lane;
+    const bool on = j < wend && m[(size_t)j * stride] != 0;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
+    if (wave == 0 && on) lst[cnt + __builtin_popcountll(bal & ((1ull << lane) - 1))] = j;
+    cnt += __builtin_popcountll(bal);
+  }
+  return cnt;
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per 128 keys
+// dK, dV: one workgroup per 128 keys, 32 per wave
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int S = D + 8, KS = D / 32, DB = D / 16, CPR = D / 8;
+  constexpr int KS = D / 16, DB = D / 32, TILE = kBQ * D, NW = 4;
+  constexpr bool kSplit = kIsBf16<T>;
   typedef typename Elt<T>::vec8 vec8;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kBQ * S];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[kBQ * S];
-  __shared__ __attribute__((aligned(16))) float sLse[kBQ];
-  __shared__ __attribute__((aligned(16))) float sD[kBQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sO0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sO1[TILE];
+  __shared__ __attribute__((aligned(16))) float sL0[kBQ];
+  __shared__ __attribute__((aligned(16))) float sL1[kBQ];
+  __shared__ __attribute__((aligned(16))) float sD0[kBQ];
+  __shared__ __attribute__((aligned(16))) float sD1[kBQ];
+  __shared__ int sList[SPARSE ? kListMax : 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5, sub = lane & 15, g4 = lane >> 4;
   int rank, bh;
   map_workgroup(blockIdx.x, p.ntiles, p.BH, &rank, &bh);
   const int kt = rank;  // causal: the lowest key tiles see the most queries, so go first
@@ -122,303 +185,338 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
   const size_t base = (size_t)bh * N * D;
   const uint16_t* Q = p.q + base;
   const uint16_t* dO = p.dO + base;
-  const float* lse = p.lse + (size_t)bh * N;
+  const float* shift = p.shift + (size_t)bh * N;
   const float* Dr = p.Dbuf + (size_t)bh * N;
   const int L = valid_keys(p.key_len, b, N);
-  const int k0 = kt * kBKV, kw = k0 + wave * 32;
+  const int k0 = kt * kBKV, kw = k0 + wave * 32, key = kw + l32;
+  const float c = p.c;
 
-  // this wave's 32 keys and values as B operands (column = key)
-  vec8 kf[2][KS], vf[2][KS];
+  // this wave's keys and values as B operands (lane = key, k = d values)
+  vec8 kf[KS], vf[KS];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int key = kw + kb * 16 + n;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[kb][ks] = as_vec8<T>(ldg16(p.k + base + (size_t)key * D + ks * 32 + g * 8, key < N));
-      vf[kb][ks] = as_vec8<T>(ldg16(p.v + base + (size_t)key * D + ks * 32 + g * 8, key < N));
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = as_vec8<T>(ldg16(p.k + base + (size_t)key * D + ks * 16 + h * 8, key < N));
+    vf[ks] = as_vec8<T>(ldg16(p.v + base + (size_t)key * D + ks * 16 + h * 8, key < N));
   }
-  f32x4 dk[DB][2], dv[DB][2];
+  f32x16 dk[DB], dv[DB];  // dK^T, dV^T: rows d = 32db + 8i + 4h + j, column = key
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      dk[db][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dv[db][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int e = 0; e < 16; ++e) dk[db][e] = dv[db][e] = 0.f;
 
-  const int nqt = (N + kBQ - 1) / kBQ;
-  int qt_begin = 0;
-  if (CAUSAL) qt_begin = k0 / kBQ;   // queries before k0 see none of these keys
-  const bool any_key = k0 < L;       // all keys padded away -> zero gradients
+  int roff[KS];  // Q / dO rows as A operands: row l32, d chunk 2 ks + h
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = tile_off<D>(l32, ks * 16 + h * 8);
+  int toff[2][DB];  // dO^T / Q^T transpose reads (rows = queries 16a + 4h + sub/4 [+8])
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      toff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec, db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
 
-  auto tile = [&](int q0) {
-    __syncthreads();
-#pragma unroll
-    for (int c = tid; c < kBQ * CPR; c += 256) {
-      const int r = c / CPR, col = (c % CPR) * 8, row = q0 + r;
-      const bool ok = row < N;
-      sts16(sQ + r * S + col, ldg16(Q + (size_t)row * D + col, ok));
-      sts16(sdO + r * S + col, ldg16(dO + (size_t)row * D + col, ok));
-    }
-    if (tid < kBQ) {
-      const int row = q0 + tid;
-      sLse[tid] = row < N ? lse_shift(lse[row]) : pos_inf();
-    } else if (tid < 2 * kBQ) {
-      const int row = q0 + tid - kBQ;
-      sD[tid - kBQ] = row < N ? Dr[row] : 0.f;
-    }
-    __syncthreads();
-    if (kw >= L) return;                            // every key of this wave is padded
-    if (CAUSAL && q0 + kBQ - 1 < kw) return;        // tile entirely before the keys
+  const TileCopy<D, kBQ, NW> copy(wave, lane);
+  const bool any_key = kw < L;  // every key of this wave padded away -> zero gradients
 
-    f32x4 s[4][2], dp[4][2];
+  auto compute = [&](const uint16_t* tq, const uint16_t* to, const float* tl, const float* td,
+                     int q0) __attribute__((always_inline)) {
+    if (!any_key) return;
+    if (CAUSAL && q0 + kBQ - 1 < kw) return;  // every query of the tile precedes the keys
+    f32x16 s[2], dp[2];  // rows = queries 32 qb + 8i + 4h + j, column = key
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb)
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int e = 0; e < 16; ++e) s[qb][e] = dp[qb][e] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const vec8 aq = as_vec8<T>(lds16(sQ + (qb * 16 + n) * S + ks * 32 + g * 8));
-        const vec8 ao = as_vec8<T>(lds16(sdO + (qb * 16 + n) * S + ks * 32 + g * 8));
+      for (int qb = 0; qb < 2; ++qb) {
+        const vec8 aq = as_vec8<T>(lds16(tq + roff[ks] + qb * 32 * D));
+        const vec8 ao = as_vec8<T>(lds16(to + roff[ks] + qb * 32 * D));
+        s[qb] = Elt<T>::mfma32(aq, kf[ks], s[qb]);
+        dp[qb] = Elt<T>::mfma32(ao, vf[ks], dp[qb]);
+      }
+    // P = exp2(c s - shift_row), dS = P (dP - D_row)
+    const bool need_mask = (kw + 32 > L) || (q0 + kBQ > N) || (CAUSAL && q0 < kw + 31);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[qb][kb] = Elt<T>::mfma(aq, kf[kb][ks], s[qb][kb]);
-          dp[qb][kb] = Elt<T>::mfma(ao, vf[kb][ks], dp[qb][kb]);
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = qb * 32 + 8 * i + 4 * h;
+        const f32x4 sh = *reinterpret_cast<const f32x4*>(tl + r);
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(td + r);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * i + j;
+          float pv = fast_exp2(fmaf(s[qb][e], c, -sh[j]));
+          if (need_mask) {
+            const int query = q0 + r + j;
+            if (key >= L || query >= N || (CAUSAL && key > query)) pv = 0.f;
+          }
+          s[qb][e] = pv;
+          dp[qb][e] = pv * (dp[qb][e] - dd[j]);
         }
       }
-
-    // P = exp2(c s - shift_row), dS = P (dP - D_row); rows = queries
-    const bool need_mask = (kw + 32 > L) || (CAUSAL && q0 < kw + 31);
+    // dV^T += dO^T P, dK^T += Q^T dS, 16 queries (chunk a) per MFMA
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const f32x4 sh = *reinterpret_cast<const f32x4*>(sLse + qb * 16 + g * 4);
-      const f32x4 dd = *reinterpret_cast<const f32x4*>(sD + qb * 16 + g * 4);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float pv = fast_exp2(fmaf(s[qb][kb][i], p.c, -sh[i]));
-          if (need_mask) {
-            const int query = q0 + qb * 16 + g * 4 + i, key = kw + kb * 16 + n;
-            if (key >= L || (CAUSAL && key > query)) pv = 0.f;
-          }
-          s[qb][kb][i] = pv;
-          dp[qb][kb][i] = pv * (dp[qb][kb][i] - dd[i]);
-        }
-    }
-
-    // dV^T += dO^T P, dK^T += Q^T dS  (k = 32 queries per MFMA).  For bf16
-    // the probabilities and dS enter as a hi + lo pair of bf16 operands: a
-    // single bf16 rounding of P (relative 2^-9) accumulated over a column
-    // costs up to ~0.01 absolute in dV, on top of the output rounding.
-    constexpr bool kSplit = kIsBf16<T>;
-#pragma unroll
-    for (int kq = 0; kq < kBQ / 32; ++kq) {
-      const int r0 = (2 * kq) * 16 + g * 4 + (n >> 2), r1 = r0 + 16;
-      vec8 pb[2], sb[2], pl[2], sl[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        pb[kb] = pack8<T>(s[2 * kq][kb], s[2 * kq + 1][kb]);
-        sb[kb] = pack8<T>(dp[2 * kq][kb], dp[2 * kq + 1][kb]);
-        if (kSplit) {
-          pl[kb] = pack8<T>(residual16<T>(s[2 * kq][kb]), residual16<T>(s[2 * kq + 1][kb]));
-          sl[kb] = pack8<T>(residual16<T>(dp[2 * kq][kb]), residual16<T>(dp[2 * kq + 1][kb]));
-        }
+    for (int a = 0; a < kBQ / 16; ++a) {
+      const vec8 pb = pack_chunk<T>(s[a >> 1], a & 1);
+      const vec8 sb = pack_chunk<T>(dp[a >> 1], a & 1);
+      vec8 pl, sl;
+      if (kSplit) {
+        pl = pack_chunk_lo<T>(s[a >> 1], a & 1);
+        sl = pack_chunk_lo<T>(dp[a >> 1], a & 1);
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int col = db * 16 + (n & 3) * 4;
-        const vec8 ao = join8<T>(lds_tr4(sdO + r0 * S + col), lds_tr4(sdO + r1 * S + col));
-        const vec8 aq = join8<T>(lds_tr4(sQ + r0 * S + col), lds_tr4(sQ + r1 * S + col));
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          dv[db][kb] = Elt<T>::mfma(ao, pb[kb], dv[db][kb]);
-          dk[db][kb] = Elt<T>::mfma(aq, sb[kb], dk[db][kb]);
-          if (kSplit) {
-            dv[db][kb] = Elt<T>::mfma(ao, pl[kb], dv[db][kb]);
-            dk[db][kb] = Elt<T>::mfma(aq, sl[kb], dk[db][kb]);
-          }
+        const vec8 ao = join8<T>(lds_tr4(to + toff[0][db] + a * 16 * D),
+                                 lds_tr4(to + toff[1][db] + a * 16 * D));
+        const vec8 aq = join8<T>(lds_tr4(tq + toff[0][db] + a * 16 * D),
+                                 lds_tr4(tq + toff[1][db] + a * 16 * D));
+        dv[db] = Elt<T>::mfma32(ao, pb, dv[db]);
+        dk[db] = Elt<T>::mfma32(aq, sb, dk[db]);
+        if (kSplit) {
+          dv[db] = Elt<T>::mfma32(ao, pl, dv[db]);
+          dk[db] = Elt<T>::mfma32(aq, sl, dk[db]);
         }
       }
     }
   };
 
-  if (any_key) {
+  // query tiles t -> first row row0(t); copies one tile ahead, one barrier per tile
+  auto walk = [&](int ntiles, auto row0) __attribute__((always_inline)) {
+    if (ntiles <= 0) return;
+    auto load = [&](int r0, uint16_t* dq_, uint16_t* do_, float* dl, float* dd)
+        __attribute__((always_inline)) {
+      copy(Q, r0, N, dq_);
+      copy(dO, r0, N, do_);
+      if (wave == 0) copy_row_stat(shift, r0, N, dl, lane);
+      if (wave == 1) copy_row_stat(Dr, r0, N, dd, lane);
+    };
+    load(row0(0), sQ0, sO0, sL0, sD0);
+    auto step = [&](int t, const uint16_t* cq, const uint16_t* co, const float* cl,
+                    const float* cd, uint16_t* nq, uint16_t* no, float* nl, float* nd)
+        __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t landed
+      __syncthreads();                     // ... and every wave's; tile t-1 fully read
+      if (t + 1 < ntiles) load(row0(t + 1), nq, no, nl, nd);
+      compute(cq, co, cl, cd, row0(t));
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1);
+      if (t + 1 < ntiles) step(t + 1, sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0);
+    }
+    __syncthreads();
+  };
+
+  if (k0 < L) {
     if (SPARSE) {
-      const int jb = kt;  // 128 keys = one mask block column
-      for (int ib = 0; ib < p.nblk; ++ib) {
-        if (!p.block_mask[(size_t)ib * p.nblk + jb]) continue;
-        for (int t = 2 * ib; t < 2 * ib + 2 && t < nqt; ++t) tile(t * kBQ);
+      const uint8_t* mcol = p.block_mask + kt;  // column kt, stride nblk
+      for (int w0 = 0; w0 < p.nblk; w0 += kListMax) {
+        const int wend = w0 + kListMax < p.nblk ? w0 + kListMax : p.nblk;
+        const int cnt = list_blocks(mcol, p.nblk, w0, wend, sList, wave, lane);
+        __syncthreads();
+        walk(2 * cnt, [&](int t) { return sList[t >> 1] * 128 + (t & 1) * kBQ; });
       }
     } else {
-      for (int t = qt_begin; t < nqt; ++t) tile(t * kBQ);
+      const int nqt = (N + kBQ - 1) / kBQ;
+      const int t0 = CAUSAL ? k0 / kBQ : 0;  // queries before k0 see none of these keys
+      walk(nqt - t0, [&](int t) { return (t0 + t) * kBQ; });
     }
   }
 
-  // store dK = scale * dK^T^T, dV (lane: key column, 4 consecutive d)
+  // store dK = scale dK^T^T and dV (4 consecutive d per store)
+  if (key < N) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int key = kw + kb * 16 + n;
-    if (key < N) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const size_t off = base + (size_t)key * D + db * 16 + g * 4;
-        *reinterpret_cast<u32x2*>(p.dk + off) = pack4<T>(dk[db][kb] * p.scale);
-        *reinterpret_cast<u32x2*>(p.dv + off) = pack4<T>(dv[db][kb]);
+      for (int i = 0; i < 4; ++i) {
+        const size_t off = base + (size_t)key * D + db * 32 + 8 * i + 4 * h;
+        const f32x4 k4 = {dk[db][4 * i] * p.scale, dk[db][4 * i + 1] * p.scale,
+                          dk[db][4 * i + 2] * p.scale, dk[db][4 * i + 3] * p.scale};
+        const f32x4 v4 = {dv[db][4 * i], dv[db][4 * i + 1], dv[db][4 * i + 2], dv[db][4 * i + 3]};
+        *reinterpret_cast<u32x2*>(p.dk + off) = pack4<T>(k4);
+        *reinterpret_cast<u32x2*>(p.dv + off) = pack4<T>(v4);
       }
-    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per 128 queries
+// dQ: one workgroup per 128 queries, 32 per wave
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams p) {
-  constexpr int S = D + 8, KS = D / 32, DB = D / 16, CPR = D / 8;
+  constexpr int KS = D / 16, DB = D / 32, TILE = kBC * D, NW = 4;
   typedef typename Elt<T>::vec8 vec8;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBC * S];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kBC * S];
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
+  __shared__ int sList[SPARSE ? kListMax : 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5, sub = lane & 15, g4 = lane >> 4;
   int rank, bh;
   map_workgroup(blockIdx.x, p.ntiles, p.BH, &rank, &bh);
-  const int qt = CAUSAL ? p.ntiles - 1 - rank : rank;
+  const int qt = CAUSAL ? p.ntiles - 1 - rank : rank;  // longest rows first
   const int b = bh / p.H, N = p.N;
   const size_t base = (size_t)bh * N * D;
   const uint16_t* K = p.k + base;
   const uint16_t* V = p.v + base;
   const int L = valid_keys(p.key_len, b, N);
-  const int q0 = qt * kBR, qw = q0 + wave * 32;
+  const int q0 = qt * kBR, qw = q0 + wave * 32, query = qw + l32;
+  const float c = p.c;
 
-  vec8 qf[2][KS], of[2][KS];
-  float sh[2], dd[2];
+  // this wave's queries and output gradients as B operands (lane = query)
+  vec8 qf[KS], of[KS];
+  const bool qok = query < N;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = qw + qb * 16 + n;
-    const bool ok = row < N;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qf[qb][ks] = as_vec8<T>(ldg16(p.q + base + (size_t)row * D + ks * 32 + g * 8, ok));
-      of[qb][ks] = as_vec8<T>(ldg16(p.dO + base + (size_t)row * D + ks * 32 + g * 8, ok));
-    }
-    sh[qb] = ok ? lse_shift(p.lse[(size_t)bh * N + row]) : pos_inf();
-    dd[qb] = ok ? p.Dbuf[(size_t)bh * N + row] : 0.f;
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = as_vec8<T>(ldg16(p.q + base + (size_t)query * D + ks * 16 + h * 8, qok));
+    of[ks] = as_vec8<T>(ldg16(p.dO + base + (size_t)query * D + ks * 16 + h * 8, qok));
   }
-  f32x4 acc[DB][2];
+  const float sh = qok ? p.shift[(size_t)bh * N + query] : pos_inf();
+  const float dd = qok ? p.Dbuf[(size_t)bh * N + query] : 0.f;
+  f32x16 acc[DB];  // dQ^T: rows d = 32db + 8i + 4h + j, column = query
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
 
-  int nkt = (L + kBC - 1) / kBC;
-  if (CAUSAL) {
-    const int last = (q0 + kBR < N ? q0 + kBR : N) - 1;
-    nkt = nkt < last / kBC + 1 ? nkt : last / kBC + 1;
-  }
-
-  auto tile = [&](int kt0) {
-    __syncthreads();
+  int roff[KS];
 #pragma unroll
-    for (int c = tid; c < kBC * CPR; c += 256) {
-      const int r = c / CPR, col = (c % CPR) * 8, key = kt0 + r;
-      const bool ok = key < N;
-      sts16(sK + r * S + col, ldg16(K + (size_t)key * D + col, ok));
-      sts16(sV + r * S + col, ldg16(V + (size_t)key * D + col, ok));
-    }
-    __syncthreads();
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = tile_off<D>(l32, ks * 16 + h * 8);
+  int toff[2][DB];
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      toff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec, db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
+
+  const TileCopy<D, kBC, NW> copy(wave, lane);
+
+  auto compute = [&](const uint16_t* tk, const uint16_t* tv, int kt0) __attribute__((always_inline)) {
     if (qw >= N) return;
-    if (CAUSAL && kt0 > qw + 31) return;
-
-    f32x4 s[4][2], dp[4][2];
+    if (CAUSAL && kt0 > qw + 31) return;  // tile above the diagonal
+    f32x16 s[2], dp[2];  // rows = keys 32 kb + 8i + 4h + j, column = query
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int e = 0; e < 16; ++e) s[kb][e] = dp[kb][e] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const vec8 ak = as_vec8<T>(lds16(sK + (kb * 16 + n) * S + ks * 32 + g * 8));
-        const vec8 av = as_vec8<T>(lds16(sV + (kb * 16 + n) * S + ks * 32 + g * 8));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          s[kb][qb] = Elt<T>::mfma(ak, qf[qb][ks], s[kb][qb]);
-          dp[kb][qb] = Elt<T>::mfma(av, of[qb][ks], dp[kb][qb]);
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        const vec8 ak = as_vec8<T>(lds16(tk + roff[ks] + kb * 32 * D));
+        const vec8 av = as_vec8<T>(lds16(tv + roff[ks] + kb * 32 * D));
+        s[kb] = Elt<T>::mfma32(ak, qf[ks], s[kb]);
+        dp[kb] = Elt<T>::mfma32(av, of[ks], dp[kb]);
       }
     const bool need_mask = (kt0 + kBC > L) || (CAUSAL && kt0 + kBC - 1 > qw);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float pv = fast_exp2(fmaf(s[kb][qb][i], p.c, -sh[qb]));
-          if (need_mask) {
-            const int key = kt0 + kb * 16 + g * 4 + i, query = qw + qb * 16 + n;
-            if (key >= L || (CAUSAL && key > query)) pv = 0.f;
-          }
-          dp[kb][qb][i] = pv * (dp[kb][qb][i] - dd[qb]);
+      for (int e = 0; e < 16; ++e) {
+        float pv = fast_exp2(fmaf(s[kb][e], c, -sh));
+        if (need_mask) {
+          const int key = kt0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (key >= L || (CAUSAL && key > query)) pv = 0.f;
         }
-    // dQ^T += K^T dS^T  (k = 32 keys per MFMA)
+        dp[kb][e] = pv * (dp[kb][e] - dd);
+      }
+    // dQ^T += K^T dS^T, 16 keys (chunk a) per MFMA
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      vec8 sb[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) sb[qb] = pack8<T>(dp[2 * kk][qb], dp[2 * kk + 1][qb]);
-      const int r0 = (2 * kk) * 16 + g * 4 + (n >> 2), r1 = r0 + 16;
+    for (int a = 0; a < kBC / 16; ++a) {
+      const vec8 sb = pack_chunk<T>(dp[a >> 1], a & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int col = db * 16 + (n & 3) * 4;
-        const vec8 a = join8<T>(lds_tr4(sK + r0 * S + col), lds_tr4(sK + r1 * S + col));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) acc[db][qb] = Elt<T>::mfma(a, sb[qb], acc[db][qb]);
+        const vec8 ak = join8<T>(lds_tr4(tk + toff[0][db] + a * 16 * D),
+                                 lds_tr4(tk + toff[1][db] + a * 16 * D));
+        acc[db] = Elt<T>::mfma32(ak, sb, acc[db]);
       }
     }
   };
 
+  auto walk = [&](int ntiles, auto key0) __attribute__((always_inline)) {
+    if (ntiles <= 0) return;
+    copy(K, key0(0), N, sK0);
+    copy(V, key0(0), N, sV0);
+    auto step = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv)
+        __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      if (t + 1 < ntiles) {
+        const int k1 = key0(t + 1);
+        copy(K, k1, N, nk);
+        copy(V, k1, N, nv);
+      }
+      compute(ck, cv, key0(t));
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, sK0, sV0, sK1, sV1);
+      if (t + 1 < ntiles) step(t + 1, sK1, sV1, sK0, sV0);
+    }
+    __syncthreads();
+  };
+
   if (SPARSE) {
     const uint8_t* mrow = p.block_mask + (size_t)qt * p.nblk;
-    for (int jb = 0; jb < p.nblk; ++jb) {
-      if (!mrow[jb]) continue;
-      for (int t = 2 * jb; t < 2 * jb + 2 && t < nkt; ++t) tile(t * kBC);
+    for (int w0 = 0; w0 < p.nblk; w0 += kListMax) {
+      const int wend = w0 + kListMax < p.nblk ? w0 + kListMax : p.nblk;
+      const int cnt = list_blocks(mrow, 1, w0, wend, sList, wave, lane);
+      __syncthreads();
+      walk(2 * cnt, [&](int t) { return sList[t >> 1] * 128 + (t & 1) * kBC; });
     }
   } else {
-    for (int t = 0; t < nkt; ++t) tile(t * kBC);
+    int nkt = (L + kBC - 1) / kBC;
+    if (CAUSAL) {
+      const int last = (q0 + kBR < N ? q0 + kBR : N) - 1;
+      nkt = nkt < last / kBC + 1 ? nkt : last / kBC + 1;
+    }
+    walk(nkt, [](int t) { return t * kBC; });
   }
 
+  if (qok) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int query = qw + qb * 16 + n;
-    if (query < N) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<u32x2*>(p.dq + base + (size_t)query * D + db * 16 + g * 4) =
-            pack4<T>(acc[db][qb] * p.scale);
-    }
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 q4 = {acc[db][4 * i] * p.scale, acc[db][4 * i + 1] * p.scale,
+                          acc[db][4 * i + 2] * p.scale, acc[db][4 * i + 3] * p.scale};
+        *reinterpret_cast<u32x2*>(p.dq + base + (size_t)query * D + db * 32 + 8 * i + 4 * h) =
+            pack4<T>(q4);
+      }
   }
 }
+
+// Every kernel the launcher below can select (the host pass of this compiler
+// otherwise leaves some kernel-template launch stubs undefined).
+#define FA_BWD_INSTANTIATE(T, D)                                                  \
+  template __global__ void bwd_pre_kernel<T, D>(const uint16_t*, const uint16_t*, \
+                                                const float*, float*, float*, int64_t); \
+  template __global__ void bwd_dkdv_kernel<T, D, true, false>(BwdParams);          \
+  template __global__ void bwd_dkdv_kernel<T, D, false, false>(BwdParams);         \
+  template __global__ void bwd_dkdv_kernel<T, D, false, true>(BwdParams);          \
+  template __global__ void bwd_dq_kernel<T, D, true, false>(BwdParams);            \
+  template __global__ void bwd_dq_kernel<T, D, false, false>(BwdParams);           \
+  template __global__ void bwd_dq_kernel<T, D, false, true>(BwdParams);
+FA_BWD_INSTANTIATE(__bf16, 64)
+FA_BWD_INSTANTIATE(__bf16, 128)
+FA_BWD_INSTANTIATE(_Float16, 64)
+FA_BWD_INSTANTIATE(_Float16, 128)
+#undef FA_BWD_INSTANTIATE
 
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 hipError_t run_bwd(const BwdArgs& a, int stage) {
   hipError_t e = hipSuccess;
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  float* Dbuf = a.workspace;
+  float* shift = a.workspace + rows;
   if (stage == 0 || stage == 1) {
-    const int64_t rows = (int64_t)a.B * a.H * a.N;
     const int64_t pre_threads = rows * (D / 8);
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((pre_threads + 255) / 256)),
                        dim3(256), 0, a.stream, static_cast<const uint16_t*>(a.o),
-                       static_cast<const uint16_t*>(a.dO), a.Dbuf, rows);
+                       static_cast<const uint16_t*>(a.dO), a.lse, Dbuf, shift, rows);
     e = hipGetLastError();
     if (e != hipSuccess || stage == 1) return e;
   }
@@ -428,8 +526,8 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   p.k = static_cast<const uint16_t*>(a.k);
   p.v = static_cast<const uint16_t*>(a.v);
   p.dO = static_cast<const uint16_t*>(a.dO);
-  p.lse = a.lse;
-  p.Dbuf = a.Dbuf;
+  p.shift = shift;
+  p.Dbuf = Dbuf;
   p.dq = static_cast<uint16_t*>(a.dq);
   p.dk = static_cast<uint16_t*>(a.dk);
   p.dv = static_cast<uint16_t*>(a.dv);
@@ -464,12 +562,14 @@ hipError_t dispatch_mask(const BwdArgs& a, int stage) {
   return a.causal ? run_bwd<T, D, true, false>(a, stage) : run_bwd<T, D, false, false>(a, stage);
 }
 
-}  // namespace
+}  // namespace bwd
 
 hipError_t launch_bwd(const BwdArgs& a, int stage) {
   if (a.dtype == 1)
-    return a.d == 64 ? dispatch_mask<_Float16, 64>(a, stage) : dispatch_mask<_Float16, 128>(a, stage);
-  return a.d == 64 ? dispatch_mask<__bf16, 64>(a, stage) : dispatch_mask<__bf16, 128>(a, stage);
+    return a.d == 64 ? bwd::dispatch_mask<_Float16, 64>(a, stage)
+                     : bwd::dispatch_mask<_Float16, 128>(a, stage);
+  return a.d == 64 ? bwd::dispatch_mask<__bf16, 64>(a, stage)
+                   : bwd::dispatch_mask<__bf16, 128>(a, stage);
 }
 
 }  // namespace fa

@@ -181,6 +181,17 @@ __device__ __forceinline__ int tile_off(int r, int c) {
   return r * D + (((c >> 3) ^ swz<D / 8>(r)) << 3) + (c & 7);
 }
 
+// Element offset, relative to row0 * D, that a copy lane reads for the tile
+// element offset `off` (tile row r = off / D) when rows at or past `nrows`
+// re-read row nrows - 1.  Signed: row0 itself may lie past nrows - 1 (the
+// second half of the last 128-row block of a block-sparse list), and the
+// result is then negative.  The row read is min(row0 + r, nrows - 1).
+__host__ __device__ inline int clamped_chunk_offset(uint32_t off, int D, int row0, int nrows) {
+  const int r = (int)(off / (uint32_t)D);
+  const int last = nrows - 1 - row0;  // last valid row, relative to row0
+  return r <= last ? (int)off : (int)off - (r - last) * D;
+}
+
 // Copies rows [row0, row0 + ROWS) of a row-major [*][D] 16-bit matrix into
 // a swizzled LDS tile with direct global->LDS loads (no VGPR staging).  NW
 // waves share the copy: 16-byte slot s of the tile (slot = 64 * instruction
@@ -215,12 +226,9 @@ struct TileCopy {
         __builtin_amdgcn_global_load_lds(base + off[j], lds + (j * NW + wave) * 512, 16, 0, 0);
     } else {
 #pragma unroll
-      for (int j = 0; j < ITER; ++j) {
-        const int r = (int)(off[j] / D);
-        const int last = nrows - 1 - row0;  // last valid row, relative to row0
-        const uint32_t o = r <= last ? off[j] : off[j] - (uint32_t)((r - last) * D);
-        __builtin_amdgcn_global_load_lds(base + o, lds + (j * NW + wave) * 512, 16, 0, 0);
-      }
+      for (int j = 0; j < ITER; ++j)
+        __builtin_amdgcn_global_load_lds(base + clamped_chunk_offset(off[j], D, row0, nrows),
+                                         lds + (j * NW + wave) * 512, 16, 0, 0);
     }
   }
 };

@@ -38,7 +38,7 @@ struct BwdArgs {
   int causal;
   const int32_t* key_len;
   const uint8_t* block_mask;
-  float* Dbuf;               // workspace: D_i = sum_c dO_ic O_ic, [B][H][N]
+  float* workspace;          // [2][B][H][N]: D_i = sum_c dO_ic O_ic, then lse_i * log2(e)
   int dtype;
   hipStream_t stream;
 };

@@ -66,8 +66,8 @@ def test_status_strings(lib):
 
 
 def test_workspace_is_linear_in_N(lib):
-    assert lib.fa_bwd_workspace_size(1, 16, 16384, 64) == 4 * 16 * 16384
-    assert lib.fa_bwd_workspace_size(2, 3, 1000, 128) == 4 * 2 * 3 * 1000
+    assert lib.fa_bwd_workspace_size(1, 16, 16384, 64) == 8 * 16 * 16384
+    assert lib.fa_bwd_workspace_size(2, 3, 1000, 128) == 8 * 2 * 3 * 1000
     assert lib.fa_bwd_workspace_size(0, 1, 1, 64) == 0
 
 
@@ -101,7 +101,7 @@ def test_fwd_validation(lib, kw, status):
 
 def bwd(lib, blocksparse=False, **kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, dO=P, dq=P, dk=P, dv=P, B=2, H=2, N=256, d=64,
-             scale=0.125, causal=0, key_len=None, ws=P, ws_bytes=4 * 2 * 2 * 256, dtype=BF16,
+             scale=0.125, causal=0, key_len=None, ws=P, ws_bytes=8 * 2 * 2 * 256, dtype=BF16,
              bm=P, bs=128)
     a.update(kw)
     if blocksparse:
@@ -116,7 +116,7 @@ def bwd(lib, blocksparse=False, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dO=None), -1), (dict(dk=None), -1), (dict(ws=None), -1),
-    (dict(ws_bytes=4 * 2 * 2 * 256 - 1), -1),     # workspace too small
+    (dict(ws_bytes=8 * 2 * 2 * 256 - 1), -1),     # workspace too small
     (dict(d=80), -2), (dict(dtype=F32), -2),
     (dict(scale=-1.0), -1), (dict(N=0), -1),
 ])
@@ -149,7 +149,7 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 def stage(lib, st, **kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, dO=P, dq=P, dk=P, dv=P, B=2, H=2, N=256, d=64,
-             scale=0.125, causal=0, key_len=None, bm=None, bs=128, ws=P, ws_bytes=4 * 2 * 2 * 256,
+             scale=0.125, causal=0, key_len=None, bm=None, bs=128, ws=P, ws_bytes=8 * 2 * 2 * 256,
              dtype=BF16)
     a.update(kw)
     return lib.fa_bwd_stage(st, a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"], a["dq"],
