@@ -71,7 +71,7 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
   if (workspace_bytes < fa_bwd_workspace_size(B, H, N, d)) return FA_ERR_INVALID;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   fa::BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
-                block_mask, static_cast<float*>(workspace), dtype,
+                block_mask, workspace, dtype,
                 static_cast<hipStream_t>(stream)};
   return hip_status(fa::launch_bwd(a, stage));
 }
@@ -89,7 +89,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
-  return size_t(8) * size_t(B) * size_t(H) * size_t(N);
+  return fa::bwd_workspace_layout(B, H, N, d).total;
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -28,6 +28,18 @@
 //             dQ^T += K^T dS^T.
 // LDS tiles are XOR-swizzled (conflict-free row and transpose reads) and
 // filled by direct global->LDS copies one tile ahead of the compute.
+//
+// bf16 inputs: the dK/dV products run on fp16 operands.  Rounding P and dS
+// to bf16 (8 significant bits) before dV = P^T dO and dK = dS^T Q costs up
+// to ~0.01 absolute in the gradients, next to the output rounding; fp16
+// keeps 11 bits.  The D pass therefore also finds max |Q|, |K|, |V|, |dO|
+// per (b, h); a convert pass writes Q * 2^-eq and dO * 2^-eo as fp16
+// (exact: every bf16 value within 2^13 of the maximum fits), and the dK/dV
+// kernel converts its K and V rows the same way.  The power-of-two
+// exponents put max |Q'|, |K'| in [2^13, 2^14) and max |dO'| in [2^3, 2^4),
+// max |V'| in [2^2, 2^3), so |dP'|, |D'| < 2^14 and |dS'| < 2^15 stay in
+// fp16 range for d <= 128; the exponents fold back exactly into the
+// softmax constant and the output scaling.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -58,35 +70,139 @@ __device__ __forceinline__ int valid_keys(const int32_t* key_len, int b, int N) 
   return kl < 0 ? 0 : (kl > N ? N : kl);
 }
 
+// Exponent e with max * 2^-e in [2^t, 2^(t+1)) for the float bit pattern
+// `maxbits` of a non-negative maximum; 0 for a zero tensor; clamped so that
+// every scale stays a normal float.
+__device__ __forceinline__ int scale_exp(uint32_t maxbits, int t) {
+  if (maxbits == 0u) return 0;
+  const int e = (int)((maxbits >> 23) & 0xffu) - 127 - t;
+  return e < -60 ? -60 : (e > 60 ? 60 : e);
+}
+constexpr int kTq = 13, kTk = 13, kTo = 3, kTv = 2;  // targets: max' in [2^t, 2^(t+1))
+
+__global__ __launch_bounds__(256) void bwd_zero_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// largest |x| of the 8 bf16 values in a 16-byte chunk, as float bits
+__device__ __forceinline__ uint32_t absmax8_bf16(u32x4 a) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = a[j] & 0x7fffu, hi = (a[j] >> 16) & 0x7fffu;
+    m = m > lo ? m : lo;
+    m = m > hi ? m : hi;
+  }
+  return m << 16;
+}
+
 // ---------------------------------------------------------------------------
 // Per row: D_i = sum_c dO_ic O_ic and shift_i = lse_i * log2(e) (+inf when
-// the row saw no key, so that exp2(c s - shift) = 0 there).
+// the row saw no key, so that exp2(c s - shift) = 0 there).  STATS (bf16
+// inputs): also max |Q|, |K|, |V|, |dO| per (b, h), into maxes[4][BH]
+// (zeroed before).  Grid (B*H, chunks of rows): a workgroup stays
+// inside one (b, h), reduces its maxima and issues one atomic max per
+// tensor, so each address sees N / kPreRows atomics.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+constexpr int kPreIter = 16;  // row groups per workgroup in the D pass
+
+template <typename T, int D, bool STATS>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const uint16_t* dO,
-                                                      const float* lse, float* Dbuf,
-                                                      float* shift, int64_t rows) {
+                                                      const float* lse, const uint16_t* q,
+                                                      const uint16_t* k, const uint16_t* v,
+                                                      float* Dbuf, float* shift,
+                                                      uint32_t* maxes, int N, int BH) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements (16 B) each
+  constexpr int RPB = 256 / TPR;  // rows per pass of the workgroup
+  const int bh = blockIdx.x;
+  const int c = (int)(threadIdx.x % TPR) * 8;
+  uint32_t mx[4] = {0u, 0u, 0u, 0u};
+  const int r_begin = blockIdx.y * RPB * kPreIter;
+#pragma unroll 4
+  for (int it = 0; it < kPreIter; ++it) {
+    const int r = r_begin + it * RPB + (int)(threadIdx.x / TPR);  // row inside this (b, h)
+    const bool ok = r < N;
+    const int64_t row = (int64_t)bh * N + r;
+    float s = 0.f;
+    if (ok) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + c);
+      const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s = fmaf(to_f32<T>(a[j] & 0xffffu), to_f32<T>(g[j] & 0xffffu), s);
+        s = fmaf(to_f32<T>(a[j] >> 16), to_f32<T>(g[j] >> 16), s);
+      }
+      if (STATS) {
+        const uint32_t m0 = absmax8_bf16(*reinterpret_cast<const u32x4*>(q + row * D + c));
+        const uint32_t m1 = absmax8_bf16(*reinterpret_cast<const u32x4*>(k + row * D + c));
+        const uint32_t m2 = absmax8_bf16(*reinterpret_cast<const u32x4*>(v + row * D + c));
+        const uint32_t m3 = absmax8_bf16(g);
+        mx[0] = mx[0] > m0 ? mx[0] : m0;
+        mx[1] = mx[1] > m1 ? mx[1] : m1;
+        mx[2] = mx[2] > m2 ? mx[2] : m2;
+        mx[3] = mx[3] > m3 ? mx[3] : m3;
+      }
+    }
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (ok && c == 0) {
+      Dbuf[row] = s;
+      const float l = lse[row];
+      shift[row] = l == neg_inf() ? pos_inf() : l * kLog2e;
+    }
+  }
+  if (STATS) {
+    __shared__ uint32_t red[4][4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t o2 = (uint32_t)__shfl_xor((int)mx[t], off);
+        mx[t] = mx[t] > o2 ? mx[t] : o2;
+      }
+    if (lane == 0)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) red[t][wave] = mx[t];
+    __syncthreads();
+    if (threadIdx.x < 4) {
+      uint32_t m = red[threadIdx.x][0];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) m = m > red[threadIdx.x][w] ? m : red[threadIdx.x][w];
+      atomicMax(maxes + (size_t)threadIdx.x * BH + bh, m);
+    }
+  }
+}
+
+// bf16 inputs: Q * 2^-eq and dO * 2^-eo as fp16, D * 2^-(eo+ev) per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, const uint16_t* dO,
+                                                          const float* Dbuf,
+                                                          const uint32_t* maxes, uint16_t* q16,
+                                                          uint16_t* do16, float* Ds,
+                                                          int64_t rows, int N, int BH) {
+  constexpr int TPR = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid / TPR;
   const int c = (int)(gid % TPR) * 8;
-  float s = 0.f;
-  if (row < rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + c);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * D + c);
+  if (row >= rows) return;
+  const int bh = (int)(row / N);
+  const int eq = scale_exp(maxes[bh], kTq), ev = scale_exp(maxes[2 * BH + bh], kTv);
+  const int eo = scale_exp(maxes[3 * BH + bh], kTo);
+  const u32x4 a = *reinterpret_cast<const u32x4*>(q + row * D + c);
+  const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + c);
+  u32x4 ra, rg;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s = fmaf(to_f32<T>(a[j] & 0xffffu), to_f32<T>(b[j] & 0xffffu), s);
-      s = fmaf(to_f32<T>(a[j] >> 16), to_f32<T>(b[j] >> 16), s);
-    }
+  for (int j = 0; j < 4; ++j) {
+    ra[j] = Elt<_Float16>::pack2(ldexpf(to_f32<__bf16>(a[j] & 0xffffu), -eq),
+                                 ldexpf(to_f32<__bf16>(a[j] >> 16), -eq));
+    rg[j] = Elt<_Float16>::pack2(ldexpf(to_f32<__bf16>(g[j] & 0xffffu), -eo),
+                                 ldexpf(to_f32<__bf16>(g[j] >> 16), -eo));
   }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (row < rows && c == 0) {
-    Dbuf[row] = s;
-    const float l = lse[row];
-    shift[row] = l == neg_inf() ? pos_inf() : l * kLog2e;
-  }
+  *reinterpret_cast<u32x4*>(q16 + row * D + c) = ra;
+  *reinterpret_cast<u32x4*>(do16 + row * D + c) = rg;
+  if (c == 0) Ds[row] = ldexpf(Dbuf[row], -(eo + ev));
 }
 
 struct BwdParams {
@@ -96,6 +212,11 @@ struct BwdParams {
   const uint16_t* dO;
   const float* shift;  // lse * log2(e), +inf for rows without keys
   const float* Dbuf;
+  // bf16 inputs, dK/dV kernel: fp16 copies, scaled D and the maxima
+  const uint16_t* q16;
+  const uint16_t* do16;
+  const float* Ds;
+  const uint32_t* maxes;
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -118,20 +239,6 @@ __device__ __forceinline__ typename Elt<T>::vec8 pack_chunk(const f32x16& x, int
   r.z = Elt<T>::pack2(x[8 * half + 4], x[8 * half + 5]);
   r.w = Elt<T>::pack2(x[8 * half + 6], x[8 * half + 7]);
   return as_vec8<T>(r);
-}
-
-// the part of the same eight values a 16-bit rounding loses
-template <typename T>
-__device__ __forceinline__ typename Elt<T>::vec8 pack_chunk_lo(const f32x16& x, int half) {
-  float r[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = x[8 * half + i] - (float)(T)x[8 * half + i];
-  u32x4 u;
-  u.x = Elt<T>::pack2(r[0], r[1]);
-  u.y = Elt<T>::pack2(r[2], r[3]);
-  u.z = Elt<T>::pack2(r[4], r[5]);
-  u.w = Elt<T>::pack2(r[6], r[7]);
-  return as_vec8<T>(u);
 }
 
 // Copy of 64 consecutive fp32 values (one per lane) into LDS, by wave 0.
@@ -160,11 +267,14 @@ __device__ __forceinline__ int list_blocks(const uint8_t* m, int stride, int w0,
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per 128 keys, 32 per wave
 // ---------------------------------------------------------------------------
+// T is the input/output type; the products always run on fp16 operands
+// (bf16 inputs: the scaled fp16 copies, see the top of this file).
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32, TILE = kBQ * D, NW = 4;
-  constexpr bool kSplit = kIsBf16<T>;
-  typedef typename Elt<T>::vec8 vec8;
+  constexpr bool kConv = kIsBf16<T>;
+  typedef _Float16 TI;
+  typedef typename Elt<TI>::vec8 vec8;
   __shared__ __attribute__((aligned(16))) uint16_t sQ0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sQ1[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sO0[TILE];
@@ -183,20 +293,38 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
   const int kt = rank;  // causal: the lowest key tiles see the most queries, so go first
   const int b = bh / p.H, N = p.N;
   const size_t base = (size_t)bh * N * D;
-  const uint16_t* Q = p.q + base;
-  const uint16_t* dO = p.dO + base;
+  const uint16_t* Q = (kConv ? p.q16 : p.q) + base;
+  const uint16_t* dO = (kConv ? p.do16 : p.dO) + base;
   const float* shift = p.shift + (size_t)bh * N;
-  const float* Dr = p.Dbuf + (size_t)bh * N;
+  const float* Dr = (kConv ? p.Ds : p.Dbuf) + (size_t)bh * N;
   const int L = valid_keys(p.key_len, b, N);
   const int k0 = kt * kBKV, kw = k0 + wave * 32, key = kw + l32;
-  const float c = p.c;
+  int eq = 0, ek = 0, ev = 0, eo = 0;  // power-of-two scales of the fp16 operands
+  if (kConv) {
+    eq = scale_exp(p.maxes[bh], kTq);
+    ek = scale_exp(p.maxes[p.BH + bh], kTk);
+    ev = scale_exp(p.maxes[2 * p.BH + bh], kTv);
+    eo = scale_exp(p.maxes[3 * p.BH + bh], kTo);
+  }
+  const float c = ldexpf(p.c, eq + ek);  // S = 2^(eq+ek) S'
 
   // this wave's keys and values as B operands (lane = key, k = d values)
   vec8 kf[KS], vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = as_vec8<T>(ldg16(p.k + base + (size_t)key * D + ks * 16 + h * 8, key < N));
-    vf[ks] = as_vec8<T>(ldg16(p.v + base + (size_t)key * D + ks * 16 + h * 8, key < N));
+    u32x4 kr = ldg16(p.k + base + (size_t)key * D + ks * 16 + h * 8, key < N);
+    u32x4 vr = ldg16(p.v + base + (size_t)key * D + ks * 16 + h * 8, key < N);
+    if (kConv) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kr[j] = Elt<TI>::pack2(ldexpf(to_f32<__bf16>(kr[j] & 0xffffu), -ek),
+                               ldexpf(to_f32<__bf16>(kr[j] >> 16), -ek));
+        vr[j] = Elt<TI>::pack2(ldexpf(to_f32<__bf16>(vr[j] & 0xffffu), -ev),
+                               ldexpf(to_f32<__bf16>(vr[j] >> 16), -ev));
+      }
+    }
+    kf[ks] = as_vec8<TI>(kr);
+    vf[ks] = as_vec8<TI>(vr);
   }
   f32x16 dk[DB], dv[DB];  // dK^T, dV^T: rows d = 32db + 8i + 4h + j, column = key
 #pragma unroll
@@ -230,10 +358,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const vec8 aq = as_vec8<T>(lds16(tq + roff[ks] + qb * 32 * D));
-        const vec8 ao = as_vec8<T>(lds16(to + roff[ks] + qb * 32 * D));
-        s[qb] = Elt<T>::mfma32(aq, kf[ks], s[qb]);
-        dp[qb] = Elt<T>::mfma32(ao, vf[ks], dp[qb]);
+        const vec8 aq = as_vec8<TI>(lds16(tq + roff[ks] + qb * 32 * D));
+        const vec8 ao = as_vec8<TI>(lds16(to + roff[ks] + qb * 32 * D));
+        s[qb] = Elt<TI>::mfma32(aq, kf[ks], s[qb]);
+        dp[qb] = Elt<TI>::mfma32(ao, vf[ks], dp[qb]);
       }
     // P = exp2(c s - shift_row), dS = P (dP - D_row)
     const bool need_mask = (kw + 32 > L) || (q0 + kBQ > N) || (CAUSAL && q0 < kw + 31);
@@ -259,25 +387,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
     // dV^T += dO^T P, dK^T += Q^T dS, 16 queries (chunk a) per MFMA
 #pragma unroll
     for (int a = 0; a < kBQ / 16; ++a) {
-      const vec8 pb = pack_chunk<T>(s[a >> 1], a & 1);
-      const vec8 sb = pack_chunk<T>(dp[a >> 1], a & 1);
-      vec8 pl, sl;
-      if (kSplit) {
-        pl = pack_chunk_lo<T>(s[a >> 1], a & 1);
-        sl = pack_chunk_lo<T>(dp[a >> 1], a & 1);
-      }
+      const vec8 pb = pack_chunk<TI>(s[a >> 1], a & 1);
+      const vec8 sb = pack_chunk<TI>(dp[a >> 1], a & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const vec8 ao = join8<T>(lds_tr4(to + toff[0][db] + a * 16 * D),
-                                 lds_tr4(to + toff[1][db] + a * 16 * D));
-        const vec8 aq = join8<T>(lds_tr4(tq + toff[0][db] + a * 16 * D),
-                                 lds_tr4(tq + toff[1][db] + a * 16 * D));
-        dv[db] = Elt<T>::mfma32(ao, pb, dv[db]);
-        dk[db] = Elt<T>::mfma32(aq, sb, dk[db]);
-        if (kSplit) {
-          dv[db] = Elt<T>::mfma32(ao, pl, dv[db]);
-          dk[db] = Elt<T>::mfma32(aq, sl, dk[db]);
-        }
+        const vec8 ao = join8<TI>(lds_tr4(to + toff[0][db] + a * 16 * D),
+                                  lds_tr4(to + toff[1][db] + a * 16 * D));
+        const vec8 aq = join8<TI>(lds_tr4(tq + toff[0][db] + a * 16 * D),
+                                  lds_tr4(tq + toff[1][db] + a * 16 * D));
+        dv[db] = Elt<TI>::mfma32(ao, pb, dv[db]);
+        dk[db] = Elt<TI>::mfma32(aq, sb, dk[db]);
       }
     }
   };
@@ -324,16 +443,20 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
     }
   }
 
-  // store dK = scale dK^T^T and dV (4 consecutive d per store)
+  // store dK = scale 2^(eq+eo+ev) dK'^T^T and dV = 2^eo dV' (4 consecutive d per store)
   if (key < N) {
+    const int ekk = eq + eo + ev;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const size_t off = base + (size_t)key * D + db * 32 + 8 * i + 4 * h;
-        const f32x4 k4 = {dk[db][4 * i] * p.scale, dk[db][4 * i + 1] * p.scale,
-                          dk[db][4 * i + 2] * p.scale, dk[db][4 * i + 3] * p.scale};
-        const f32x4 v4 = {dv[db][4 * i], dv[db][4 * i + 1], dv[db][4 * i + 2], dv[db][4 * i + 3]};
+        f32x4 k4, v4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          k4[j] = ldexpf(dk[db][4 * i + j] * p.scale, ekk);
+          v4[j] = ldexpf(dv[db][4 * i + j], eo);
+        }
         *reinterpret_cast<u32x2*>(p.dk + off) = pack4<T>(k4);
         *reinterpret_cast<u32x2*>(p.dv + off) = pack4<T>(v4);
       }
@@ -492,8 +615,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
 // Every kernel the launcher below can select (the host pass of this compiler
 // otherwise leaves some kernel-template launch stubs undefined).
 #define FA_BWD_INSTANTIATE(T, D)                                                  \
-  template __global__ void bwd_pre_kernel<T, D>(const uint16_t*, const uint16_t*, \
-                                                const float*, float*, float*, int64_t); \
+  template __global__ void bwd_pre_kernel<T, D, kIsBf16<T>>(                      \
+      const uint16_t*, const uint16_t*, const float*, const uint16_t*, const uint16_t*, \
+      const uint16_t*, float*, float*, uint32_t*, int, int);                        \
   template __global__ void bwd_dkdv_kernel<T, D, true, false>(BwdParams);          \
   template __global__ void bwd_dkdv_kernel<T, D, false, false>(BwdParams);         \
   template __global__ void bwd_dkdv_kernel<T, D, false, true>(BwdParams);          \
@@ -505,19 +629,49 @@ FA_BWD_INSTANTIATE(__bf16, 128)
 FA_BWD_INSTANTIATE(_Float16, 64)
 FA_BWD_INSTANTIATE(_Float16, 128)
 #undef FA_BWD_INSTANTIATE
+template __global__ void bwd_convert_kernel<64>(const uint16_t*, const uint16_t*, const float*,
+                                                const uint32_t*, uint16_t*, uint16_t*, float*,
+                                                int64_t, int, int);
+template __global__ void bwd_convert_kernel<128>(const uint16_t*, const uint16_t*, const float*,
+                                                 const uint32_t*, uint16_t*, uint16_t*, float*,
+                                                 int64_t, int, int);
 
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 hipError_t run_bwd(const BwdArgs& a, int stage) {
+  constexpr bool kConv = kIsBf16<T>;
   hipError_t e = hipSuccess;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
-  float* Dbuf = a.workspace;
-  float* shift = a.workspace + rows;
+  const int BH = a.B * a.H;
+  const BwdWorkspace w = bwd_workspace_layout(a.B, a.H, a.N, a.d);
+  char* ws = static_cast<char*>(a.workspace);
+  float* Dbuf = reinterpret_cast<float*>(ws + w.D);
+  float* shift = reinterpret_cast<float*>(ws + w.shift);
+  float* Ds = reinterpret_cast<float*>(ws + w.Ds);
+  uint32_t* maxes = reinterpret_cast<uint32_t*>(ws + w.maxes);
+  uint16_t* q16 = reinterpret_cast<uint16_t*>(ws + w.q16);
+  uint16_t* do16 = reinterpret_cast<uint16_t*>(ws + w.do16);
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* dO = static_cast<const uint16_t*>(a.dO);
   if (stage == 0 || stage == 1) {
-    const int64_t pre_threads = rows * (D / 8);
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((pre_threads + 255) / 256)),
-                       dim3(256), 0, a.stream, static_cast<const uint16_t*>(a.o),
-                       static_cast<const uint16_t*>(a.dO), a.lse, Dbuf, shift, rows);
+    const unsigned row_blocks = (unsigned)((rows * (D / 8) + 255) / 256);
+    if (kConv) {
+      hipLaunchKernelGGL(bwd_zero_kernel, dim3((4 * BH + 255) / 256), dim3(256), 0, a.stream,
+                         maxes, 4 * BH);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    constexpr int pre_rows = 256 / (D / 8) * kPreIter;  // rows per workgroup
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D, kConv>), dim3(BH, (a.N + pre_rows - 1) / pre_rows),
+                       dim3(256), 0, a.stream, static_cast<const uint16_t*>(a.o), dO, a.lse, q,
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), Dbuf,
+                       shift, maxes, a.N, BH);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (kConv) {
+      hipLaunchKernelGGL((bwd_convert_kernel<D>), dim3(row_blocks), dim3(256), 0, a.stream, q, dO,
+                         Dbuf, maxes, q16, do16, Ds, rows, a.N, BH);
+      e = hipGetLastError();
+    }
     if (e != hipSuccess || stage == 1) return e;
   }
 
@@ -528,6 +682,10 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   p.dO = static_cast<const uint16_t*>(a.dO);
   p.shift = shift;
   p.Dbuf = Dbuf;
+  p.q16 = q16;
+  p.do16 = do16;
+  p.Ds = Ds;
+  p.maxes = maxes;
   p.dq = static_cast<uint16_t*>(a.dq);
   p.dk = static_cast<uint16_t*>(a.dk);
   p.dv = static_cast<uint16_t*>(a.dv);

@@ -38,10 +38,38 @@ struct BwdArgs {
   int causal;
   const int32_t* key_len;
   const uint8_t* block_mask;
-  float* workspace;          // [2][B][H][N]: D_i = sum_c dO_ic O_ic, then lse_i * log2(e)
+  void* workspace;           // bwd_workspace_layout(B, H, N, d).total bytes
   int dtype;
   hipStream_t stream;
 };
+
+// Backward workspace, regions 256-byte aligned, in this order:
+//   D      f32 [BHN]      D_i = sum_c dO_ic O_ic
+//   shift  f32 [BHN]      lse_i * log2(e), +inf for rows without keys
+//   Ds     f32 [BHN]      D_i * 2^-(eo+ev)          (bf16 inputs)
+//   maxes  u32 [4][BH]    max |Q|, |K|, |V|, |dO| per (b, h), float bits (bf16 inputs)
+//   q16    f16 [BHN d]    Q * 2^-eq                 (bf16 inputs)
+//   do16   f16 [BHN d]    dO * 2^-eo                (bf16 inputs)
+// (BHN = B*H*N; eq, eo, ev are the per-(b, h) power-of-two exponents that
+// the kernels derive from the maxima.)
+struct BwdWorkspace {
+  size_t D, shift, Ds, maxes, q16, do16, total;
+};
+
+inline size_t ws_align(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline BwdWorkspace bwd_workspace_layout(int64_t B, int64_t H, int64_t N, int64_t d) {
+  const size_t bhn = size_t(B * H * N), bh = size_t(B * H);
+  BwdWorkspace w;
+  w.D = 0;
+  w.shift = ws_align(w.D + 4 * bhn);
+  w.Ds = ws_align(w.shift + 4 * bhn);
+  w.maxes = ws_align(w.Ds + 4 * bhn);
+  w.q16 = ws_align(w.maxes + 16 * bh);
+  w.do16 = ws_align(w.q16 + 2 * bhn * size_t(d));
+  w.total = ws_align(w.do16 + 2 * bhn * size_t(d));
+  return w;
+}
 
 hipError_t launch_fwd(const FwdArgs& a);
 // stage 0: all three launches; 1: D only; 2: dK/dV only; 3: dQ only

@@ -65,15 +65,28 @@ def test_status_strings(lib):
     assert lib.fa_status_string(7) == b"unknown status"
 
 
+def ws_formula(B, H, N, d):
+    # per query row: D, shift, scaled D (3 floats) and the fp16 copies of its
+    # q and dO rows (4 d bytes); per (b, h): four maxima; 256-byte alignment
+    # of six regions
+    return 12 * B * H * N + 4 * B * H * N * d + 16 * B * H
+
+
 def test_workspace_is_linear_in_N(lib):
-    assert lib.fa_bwd_workspace_size(1, 16, 16384, 64) == 8 * 16 * 16384
-    assert lib.fa_bwd_workspace_size(2, 3, 1000, 128) == 8 * 2 * 3 * 1000
+    for B, H, N, d in [(1, 16, 16384, 64), (2, 3, 1000, 128), (1, 1, 1, 64)]:
+        got = lib.fa_bwd_workspace_size(B, H, N, d)
+        assert ws_formula(B, H, N, d) <= got < ws_formula(B, H, N, d) + 6 * 256
+        assert got % 256 == 0
+    a, b = lib.fa_bwd_workspace_size(1, 16, 8192, 64), lib.fa_bwd_workspace_size(1, 16, 16384, 64)
+    assert abs(b - 2 * a) <= 6 * 256
+    assert lib.fa_bwd_workspace_size(2, 2, 256, 64) == WS
     assert lib.fa_bwd_workspace_size(0, 1, 1, 64) == 0
 
 
 # Fake, never-dereferenced, 16-byte aligned "device" addresses: validation
 # rejects every call below before anything touches them.
 P = 0x100000
+WS = 274688  # fa_bwd_workspace_size(2, 2, 256, 64), checked below
 F16, BF16, F32 = 1, 2, 0
 
 
@@ -101,7 +114,7 @@ def test_fwd_validation(lib, kw, status):
 
 def bwd(lib, blocksparse=False, **kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, dO=P, dq=P, dk=P, dv=P, B=2, H=2, N=256, d=64,
-             scale=0.125, causal=0, key_len=None, ws=P, ws_bytes=8 * 2 * 2 * 256, dtype=BF16,
+             scale=0.125, causal=0, key_len=None, ws=P, ws_bytes=WS, dtype=BF16,
              bm=P, bs=128)
     a.update(kw)
     if blocksparse:
@@ -116,7 +129,7 @@ def bwd(lib, blocksparse=False, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dO=None), -1), (dict(dk=None), -1), (dict(ws=None), -1),
-    (dict(ws_bytes=8 * 2 * 2 * 256 - 1), -1),     # workspace too small
+    (dict(ws_bytes=WS - 1), -1),                  # workspace too small
     (dict(d=80), -2), (dict(dtype=F32), -2),
     (dict(scale=-1.0), -1), (dict(N=0), -1),
 ])
@@ -149,7 +162,7 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 def stage(lib, st, **kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, dO=P, dq=P, dk=P, dv=P, B=2, H=2, N=256, d=64,
-             scale=0.125, causal=0, key_len=None, bm=None, bs=128, ws=P, ws_bytes=8 * 2 * 2 * 256,
+             scale=0.125, causal=0, key_len=None, bm=None, bs=128, ws=P, ws_bytes=WS,
              dtype=BF16)
     a.update(kw)
     return lib.fa_bwd_stage(st, a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"], a["dq"],
