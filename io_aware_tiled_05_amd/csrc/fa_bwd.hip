@@ -29,17 +29,21 @@
 // LDS tiles are XOR-swizzled (conflict-free row and transpose reads) and
 // filled by direct global->LDS copies one tile ahead of the compute.
 //
-// bf16 inputs: the dK/dV products run on fp16 operands.  Rounding P and dS
-// to bf16 (8 significant bits) before dV = P^T dO and dK = dS^T Q costs up
-// to ~0.01 absolute in the gradients, next to the output rounding; fp16
-// keeps 11 bits.  The D pass therefore also finds max |Q|, |K|, |V|, |dO|
-// per (b, h); a convert pass writes Q * 2^-eq and dO * 2^-eo as fp16
-// (exact: every bf16 value within 2^13 of the maximum fits), and the dK/dV
-// kernel converts its K and V rows the same way.  The power-of-two
-// exponents put max |Q'|, |K'| in [2^13, 2^14) and max |dO'| in [2^3, 2^4),
-// max |V'| in [2^2, 2^3), so |dP'|, |D'| < 2^14 and |dS'| < 2^15 stay in
-// fp16 range for d <= 128; the exponents fold back exactly into the
-// softmax constant and the output scaling.
+// The dK/dV products run on fp16 operands for both input types.  Rounding
+// P and dS to bf16 (8 significant bits) before dV = P^T dO and dK = dS^T Q
+// costs up to ~0.01 absolute in the gradients, next to the output
+// rounding; fp16 keeps 11 bits.  The D pass also finds max |Q|, |K|, |V|,
+// |dO| per (b, h); a convert pass writes c Q * 2^-eq (c = scale * log2 e)
+// and dO * 2^-eo as fp16, and -shift * 2^-f, -D * 2^-(eo+ev) per row; the
+// dK/dV kernel converts its K and V rows the same way (* 2^-ek, * 2^-ev).
+// The power-of-two exponents keep every operand in fp16 range (max |dO'|
+// in [2^3, 2^4), |V'| in [2^2, 2^3), so |dP'|, |D'| < 2^14 and |dS'| < 2^15
+// for d <= 128; |c Q'|, |K'| <= 2^14) and fold back exactly into the output
+// scaling.  eq and ek are split so that f = eq + ek = 0 whenever the
+// geometric mean of max |c Q| and max |K| lies in [2^-4, 2^13]: then the
+// score accumulator, started at -shift, is exactly the exponent of P, and
+// the dP accumulator, started at -D, is exactly dP - D, so P costs one
+// exponential and dS one multiply.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -80,13 +84,47 @@ __device__ __forceinline__ int scale_exp(uint32_t maxbits, int t) {
 }
 constexpr int kTq = 13, kTk = 13, kTo = 3, kTv = 2;  // targets: max' in [2^t, 2^(t+1))
 
+__device__ __forceinline__ int exp_of(uint32_t bits) { return (int)((bits >> 23) & 0xffu) - 127; }
+__device__ __forceinline__ int clamp60(int e) { return e < -60 ? -60 : (e > 60 ? 60 : e); }
+
+// Per-(b, h) exponents of the fp16 operands of the dK/dV products:
+// Q'' = c Q 2^-eq, K' = K 2^-ek, V' = V 2^-ev, dO' = dO 2^-eo, c S = 2^f S''.
+struct Scales {
+  int eq, ek, ev, eo, f;
+};
+
+__device__ __forceinline__ Scales bwd_scales(const uint32_t* maxes, int BH, int bh, float c) {
+  Scales s;
+  const uint32_t mq = __builtin_bit_cast(uint32_t, c * __builtin_bit_cast(float, maxes[bh]));
+  const uint32_t mk = maxes[BH + bh];
+  s.ev = scale_exp(maxes[2 * BH + bh], kTv);
+  s.eo = scale_exp(maxes[3 * BH + bh], kTo);
+  if (mq == 0u || mk == 0u) {
+    s.eq = s.ek = 0;
+  } else {
+    const int Eq = exp_of(mq), Ek = exp_of(mk), g = Eq + Ek;
+    if (g >= -8 && g <= 26) {  // balanced: both maxima near 2^(g/2), eq + ek = 0
+      const int d = Eq - Ek;
+      s.eq = clamp60(d >= 0 ? d / 2 : -((-d + 1) / 2));  // floor(d / 2)
+      s.ek = -s.eq;
+    } else {
+      s.eq = clamp60(Eq - kTq);
+      s.ek = clamp60(Ek - kTk);
+    }
+  }
+  s.f = s.eq + s.ek;
+  return s;
+}
+
 __global__ __launch_bounds__(256) void bwd_zero_kernel(uint32_t* p, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0u;
 }
 
-// largest |x| of the 8 bf16 values in a 16-byte chunk, as float bits
-__device__ __forceinline__ uint32_t absmax8_bf16(u32x4 a) {
+// largest |x| of the 8 16-bit values in a 16-byte chunk, as float bits
+// (magnitude bit patterns of both formats order like the values)
+template <typename T>
+__device__ __forceinline__ uint32_t absmax8(u32x4 a) {
   uint32_t m = 0u;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -94,7 +132,7 @@ __device__ __forceinline__ uint32_t absmax8_bf16(u32x4 a) {
     m = m > lo ? m : lo;
     m = m > hi ? m : hi;
   }
-  return m << 16;
+  return __builtin_bit_cast(uint32_t, to_f32<T>(m));
 }
 
 // ---------------------------------------------------------------------------
@@ -134,10 +172,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
         s = fmaf(to_f32<T>(a[j] >> 16), to_f32<T>(g[j] >> 16), s);
       }
       if (STATS) {
-        const uint32_t m0 = absmax8_bf16(*reinterpret_cast<const u32x4*>(q + row * D + c));
-        const uint32_t m1 = absmax8_bf16(*reinterpret_cast<const u32x4*>(k + row * D + c));
-        const uint32_t m2 = absmax8_bf16(*reinterpret_cast<const u32x4*>(v + row * D + c));
-        const uint32_t m3 = absmax8_bf16(g);
+        const uint32_t m0 = absmax8<T>(*reinterpret_cast<const u32x4*>(q + row * D + c));
+        const uint32_t m1 = absmax8<T>(*reinterpret_cast<const u32x4*>(k + row * D + c));
+        const uint32_t m2 = absmax8<T>(*reinterpret_cast<const u32x4*>(v + row * D + c));
+        const uint32_t m3 = absmax8<T>(g);
         mx[0] = mx[0] > m0 ? mx[0] : m0;
         mx[1] = mx[1] > m1 ? mx[1] : m1;
         mx[2] = mx[2] > m2 ? mx[2] : m2;
@@ -175,34 +213,38 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
   }
 }
 
-// bf16 inputs: Q * 2^-eq and dO * 2^-eo as fp16, D * 2^-(eo+ev) per row.
-template <int D>
+// c Q * 2^-eq and dO * 2^-eo as fp16; -shift * 2^-f and -D * 2^-(eo+ev)
+// per row (the initial values of the dK/dV kernel's score and dP
+// accumulators).
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, const uint16_t* dO,
-                                                          const float* Dbuf,
-                                                          const uint32_t* maxes, uint16_t* q16,
-                                                          uint16_t* do16, float* Ds,
-                                                          int64_t rows, int N, int BH) {
+                                                          const float* Dbuf, const float* shift,
+                                                          const uint32_t* maxes, float c,
+                                                          uint16_t* q16, uint16_t* do16,
+                                                          float* nDs, float* nsh, int64_t rows,
+                                                          int N, int BH) {
   constexpr int TPR = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid / TPR;
-  const int c = (int)(gid % TPR) * 8;
+  const int col = (int)(gid % TPR) * 8;
   if (row >= rows) return;
-  const int bh = (int)(row / N);
-  const int eq = scale_exp(maxes[bh], kTq), ev = scale_exp(maxes[2 * BH + bh], kTv);
-  const int eo = scale_exp(maxes[3 * BH + bh], kTo);
-  const u32x4 a = *reinterpret_cast<const u32x4*>(q + row * D + c);
-  const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + c);
+  const Scales sc = bwd_scales(maxes, BH, (int)(row / N), c);
+  const float cq = ldexpf(c, -sc.eq);
+  const u32x4 a = *reinterpret_cast<const u32x4*>(q + row * D + col);
+  const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + col);
   u32x4 ra, rg;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    ra[j] = Elt<_Float16>::pack2(ldexpf(to_f32<__bf16>(a[j] & 0xffffu), -eq),
-                                 ldexpf(to_f32<__bf16>(a[j] >> 16), -eq));
-    rg[j] = Elt<_Float16>::pack2(ldexpf(to_f32<__bf16>(g[j] & 0xffffu), -eo),
-                                 ldexpf(to_f32<__bf16>(g[j] >> 16), -eo));
+    ra[j] = Elt<_Float16>::pack2(cq * to_f32<T>(a[j] & 0xffffu), cq * to_f32<T>(a[j] >> 16));
+    rg[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(g[j] & 0xffffu), -sc.eo),
+                                 ldexpf(to_f32<T>(g[j] >> 16), -sc.eo));
   }
-  *reinterpret_cast<u32x4*>(q16 + row * D + c) = ra;
-  *reinterpret_cast<u32x4*>(do16 + row * D + c) = rg;
-  if (c == 0) Ds[row] = ldexpf(Dbuf[row], -(eo + ev));
+  *reinterpret_cast<u32x4*>(q16 + row * D + col) = ra;
+  *reinterpret_cast<u32x4*>(do16 + row * D + col) = rg;
+  if (col == 0) {
+    nDs[row] = -ldexpf(Dbuf[row], -(sc.eo + sc.ev));
+    nsh[row] = -ldexpf(shift[row], -sc.f);
+  }
 }
 
 struct BwdParams {
@@ -212,10 +254,11 @@ struct BwdParams {
   const uint16_t* dO;
   const float* shift;  // lse * log2(e), +inf for rows without keys
   const float* Dbuf;
-  // bf16 inputs, dK/dV kernel: fp16 copies, scaled D and the maxima
+  // dK/dV kernel: fp16 copies, negated scaled D and shift, the maxima
   const uint16_t* q16;
   const uint16_t* do16;
-  const float* Ds;
+  const float* nDs;
+  const float* nsh;
   const uint32_t* maxes;
   uint16_t* dq;
   uint16_t* dk;
@@ -267,12 +310,11 @@ __device__ __forceinline__ int list_blocks(const uint8_t* m, int stride, int w0,
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per 128 keys, 32 per wave
 // ---------------------------------------------------------------------------
-// T is the input/output type; the products always run on fp16 operands
-// (bf16 inputs: the scaled fp16 copies, see the top of this file).
+// T is the input/output type; the products run on the scaled fp16 operands
+// described at the top of this file.
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32, TILE = kBQ * D, NW = 4;
-  constexpr bool kConv = kIsBf16<T>;
   typedef _Float16 TI;
   typedef typename Elt<TI>::vec8 vec8;
   __shared__ __attribute__((aligned(16))) uint16_t sQ0[TILE];
@@ -293,20 +335,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
   const int kt = rank;  // causal: the lowest key tiles see the most queries, so go first
   const int b = bh / p.H, N = p.N;
   const size_t base = (size_t)bh * N * D;
-  const uint16_t* Q = (kConv ? p.q16 : p.q) + base;
-  const uint16_t* dO = (kConv ? p.do16 : p.dO) + base;
-  const float* shift = p.shift + (size_t)bh * N;
-  const float* Dr = (kConv ? p.Ds : p.Dbuf) + (size_t)bh * N;
+  const uint16_t* Q = p.q16 + base;    // c Q 2^-eq
+  const uint16_t* dO = p.do16 + base;  // dO 2^-eo
+  const float* nsh = p.nsh + (size_t)bh * N;
+  const float* nD = p.nDs + (size_t)bh * N;
   const int L = valid_keys(p.key_len, b, N);
   const int k0 = kt * kBKV, kw = k0 + wave * 32, key = kw + l32;
-  int eq = 0, ek = 0, ev = 0, eo = 0;  // power-of-two scales of the fp16 operands
-  if (kConv) {
-    eq = scale_exp(p.maxes[bh], kTq);
-    ek = scale_exp(p.maxes[p.BH + bh], kTk);
-    ev = scale_exp(p.maxes[2 * p.BH + bh], kTv);
-    eo = scale_exp(p.maxes[3 * p.BH + bh], kTo);
-  }
-  const float c = ldexpf(p.c, eq + ek);  // S = 2^(eq+ek) S'
+  const Scales sc = bwd_scales(p.maxes, p.BH, bh, p.c);
+  const int ek = sc.ek, ev = sc.ev;
 
   // this wave's keys and values as B operands (lane = key, k = d values)
   vec8 kf[KS], vf[KS];
@@ -314,14 +350,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 kr = ldg16(p.k + base + (size_t)key * D + ks * 16 + h * 8, key < N);
     u32x4 vr = ldg16(p.v + base + (size_t)key * D + ks * 16 + h * 8, key < N);
-    if (kConv) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kr[j] = Elt<TI>::pack2(ldexpf(to_f32<__bf16>(kr[j] & 0xffffu), -ek),
-                               ldexpf(to_f32<__bf16>(kr[j] >> 16), -ek));
-        vr[j] = Elt<TI>::pack2(ldexpf(to_f32<__bf16>(vr[j] & 0xffffu), -ev),
-                               ldexpf(to_f32<__bf16>(vr[j] >> 16), -ev));
-      }
+    for (int j = 0; j < 4; ++j) {
+      kr[j] = Elt<TI>::pack2(ldexpf(to_f32<T>(kr[j] & 0xffffu), -ek),
+                             ldexpf(to_f32<T>(kr[j] >> 16), -ek));
+      vr[j] = Elt<TI>::pack2(ldexpf(to_f32<T>(vr[j] & 0xffffu), -ev),
+                             ldexpf(to_f32<T>(vr[j] >> 16), -ev));
     }
     kf[ks] = as_vec8<TI>(kr);
     vf[ks] = as_vec8<TI>(vr);
@@ -349,11 +383,23 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
                      int q0) __attribute__((always_inline)) {
     if (!any_key) return;
     if (CAUSAL && q0 + kBQ - 1 < kw) return;  // every query of the tile precedes the keys
-    f32x16 s[2], dp[2];  // rows = queries 32 qb + 8i + 4h + j, column = key
+    // rows = queries 32 qb + 8i + 4h + j, column = key.  The score
+    // accumulator starts at -shift 2^-f and the dP accumulator at
+    // -D 2^-(eo+ev) (the row's values, read in accumulator order), so they
+    // end as 2^-f (c s - shift) and 2^-(eo+ev) (dP - D).
+    f32x16 s[2], dp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[qb][e] = dp[qb][e] = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(tl + qb * 32 + 8 * i + 4 * h);
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(td + qb * 32 + 8 * i + 4 * h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s[qb][4 * i + j] = a4[j];
+          dp[qb][4 * i + j] = b4[j];
+        }
+      }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -363,26 +409,24 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
         s[qb] = Elt<TI>::mfma32(aq, kf[ks], s[qb]);
         dp[qb] = Elt<TI>::mfma32(ao, vf[ks], dp[qb]);
       }
-    // P = exp2(c s - shift_row), dS = P (dP - D_row)
+    // P = exp2(c s - shift_row), dS' = P (dP - D_row) 2^-(eo+ev)
     const bool need_mask = (kw + 32 > L) || (q0 + kBQ > N) || (CAUSAL && q0 < kw + 31);
+    if (sc.f != 0) {  // unbalanced operand scales (extreme input ranges only)
+      const float sf = ldexpf(1.f, sc.f);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[qb] *= sf;
+    }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = qb * 32 + 8 * i + 4 * h;
-        const f32x4 sh = *reinterpret_cast<const f32x4*>(tl + r);
-        const f32x4 dd = *reinterpret_cast<const f32x4*>(td + r);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 4 * i + j;
-          float pv = fast_exp2(fmaf(s[qb][e], c, -sh[j]));
-          if (need_mask) {
-            const int query = q0 + r + j;
-            if (key >= L || query >= N || (CAUSAL && key > query)) pv = 0.f;
-          }
-          s[qb][e] = pv;
-          dp[qb][e] = pv * (dp[qb][e] - dd[j]);
+      for (int e = 0; e < 16; ++e) {
+        float pv = fast_exp2(s[qb][e]);
+        if (need_mask) {
+          const int query = q0 + qb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (key >= L || query >= N || (CAUSAL && key > query)) pv = 0.f;
         }
+        s[qb][e] = pv;
+        dp[qb][e] *= pv;
       }
     // dV^T += dO^T P, dK^T += Q^T dS, 16 queries (chunk a) per MFMA
 #pragma unroll
@@ -408,8 +452,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
         __attribute__((always_inline)) {
       copy(Q, r0, N, dq_);
       copy(dO, r0, N, do_);
-      if (wave == 0) copy_row_stat(shift, r0, N, dl, lane);
-      if (wave == 1) copy_row_stat(Dr, r0, N, dd, lane);
+      if (wave == 0) copy_row_stat(nsh, r0, N, dl, lane);
+      if (wave == 1) copy_row_stat(nD, r0, N, dd, lane);
     };
     load(row0(0), sQ0, sO0, sL0, sD0);
     auto step = [&](int t, const uint16_t* cq, const uint16_t* co, const float* cl,
@@ -443,9 +487,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
     }
   }
 
-  // store dK = scale 2^(eq+eo+ev) dK'^T^T and dV = 2^eo dV' (4 consecutive d per store)
+  // store dK = scale/c 2^(eq+eo+ev) dK'^T^T (scale/c = ln 2) and dV = 2^eo dV'
+  // (4 consecutive d per store)
   if (key < N) {
-    const int ekk = eq + eo + ev;
+    const int ekk = sc.eq + sc.eo + sc.ev;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -454,8 +499,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
         f32x4 k4, v4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          k4[j] = ldexpf(dk[db][4 * i + j] * p.scale, ekk);
-          v4[j] = ldexpf(dv[db][4 * i + j], eo);
+          k4[j] = ldexpf(dk[db][4 * i + j] * kLn2, ekk);
+          v4[j] = ldexpf(dv[db][4 * i + j], sc.eo);
         }
         *reinterpret_cast<u32x2*>(p.dk + off) = pack4<T>(k4);
         *reinterpret_cast<u32x2*>(p.dv + off) = pack4<T>(v4);
@@ -615,7 +660,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
 // Every kernel the launcher below can select (the host pass of this compiler
 // otherwise leaves some kernel-template launch stubs undefined).
 #define FA_BWD_INSTANTIATE(T, D)                                                  \
-  template __global__ void bwd_pre_kernel<T, D, kIsBf16<T>>(                      \
+  template __global__ void bwd_pre_kernel<T, D, true>(                            \
       const uint16_t*, const uint16_t*, const float*, const uint16_t*, const uint16_t*, \
       const uint16_t*, float*, float*, uint32_t*, int, int);                        \
   template __global__ void bwd_dkdv_kernel<T, D, true, false>(BwdParams);          \
@@ -623,22 +668,18 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
   template __global__ void bwd_dkdv_kernel<T, D, false, true>(BwdParams);          \
   template __global__ void bwd_dq_kernel<T, D, true, false>(BwdParams);            \
   template __global__ void bwd_dq_kernel<T, D, false, false>(BwdParams);           \
-  template __global__ void bwd_dq_kernel<T, D, false, true>(BwdParams);
+  template __global__ void bwd_dq_kernel<T, D, false, true>(BwdParams);          \
+  template __global__ void bwd_convert_kernel<T, D>(                               \
+      const uint16_t*, const uint16_t*, const float*, const float*, const uint32_t*, float, \
+      uint16_t*, uint16_t*, float*, float*, int64_t, int, int);
 FA_BWD_INSTANTIATE(__bf16, 64)
 FA_BWD_INSTANTIATE(__bf16, 128)
 FA_BWD_INSTANTIATE(_Float16, 64)
 FA_BWD_INSTANTIATE(_Float16, 128)
 #undef FA_BWD_INSTANTIATE
-template __global__ void bwd_convert_kernel<64>(const uint16_t*, const uint16_t*, const float*,
-                                                const uint32_t*, uint16_t*, uint16_t*, float*,
-                                                int64_t, int, int);
-template __global__ void bwd_convert_kernel<128>(const uint16_t*, const uint16_t*, const float*,
-                                                 const uint32_t*, uint16_t*, uint16_t*, float*,
-                                                 int64_t, int, int);
 
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 hipError_t run_bwd(const BwdArgs& a, int stage) {
-  constexpr bool kConv = kIsBf16<T>;
   hipError_t e = hipSuccess;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   const int BH = a.B * a.H;
@@ -646,7 +687,9 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   char* ws = static_cast<char*>(a.workspace);
   float* Dbuf = reinterpret_cast<float*>(ws + w.D);
   float* shift = reinterpret_cast<float*>(ws + w.shift);
-  float* Ds = reinterpret_cast<float*>(ws + w.Ds);
+  float* nDs = reinterpret_cast<float*>(ws + w.nDs);
+  float* nsh = reinterpret_cast<float*>(ws + w.nsh);
+  const float c = a.scale * kLog2e;
   uint32_t* maxes = reinterpret_cast<uint32_t*>(ws + w.maxes);
   uint16_t* q16 = reinterpret_cast<uint16_t*>(ws + w.q16);
   uint16_t* do16 = reinterpret_cast<uint16_t*>(ws + w.do16);
@@ -654,24 +697,20 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   const uint16_t* dO = static_cast<const uint16_t*>(a.dO);
   if (stage == 0 || stage == 1) {
     const unsigned row_blocks = (unsigned)((rows * (D / 8) + 255) / 256);
-    if (kConv) {
-      hipLaunchKernelGGL(bwd_zero_kernel, dim3((4 * BH + 255) / 256), dim3(256), 0, a.stream,
-                         maxes, 4 * BH);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3((4 * BH + 255) / 256), dim3(256), 0, a.stream,
+                       maxes, 4 * BH);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     constexpr int pre_rows = 256 / (D / 8) * kPreIter;  // rows per workgroup
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D, kConv>), dim3(BH, (a.N + pre_rows - 1) / pre_rows),
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D, true>), dim3(BH, (a.N + pre_rows - 1) / pre_rows),
                        dim3(256), 0, a.stream, static_cast<const uint16_t*>(a.o), dO, a.lse, q,
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), Dbuf,
                        shift, maxes, a.N, BH);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (kConv) {
-      hipLaunchKernelGGL((bwd_convert_kernel<D>), dim3(row_blocks), dim3(256), 0, a.stream, q, dO,
-                         Dbuf, maxes, q16, do16, Ds, rows, a.N, BH);
-      e = hipGetLastError();
-    }
+    hipLaunchKernelGGL((bwd_convert_kernel<T, D>), dim3(row_blocks), dim3(256), 0, a.stream, q,
+                       dO, Dbuf, shift, maxes, c, q16, do16, nDs, nsh, rows, a.N, BH);
+    e = hipGetLastError();
     if (e != hipSuccess || stage == 1) return e;
   }
 
@@ -684,7 +723,8 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   p.Dbuf = Dbuf;
   p.q16 = q16;
   p.do16 = do16;
-  p.Ds = Ds;
+  p.nDs = nDs;
+  p.nsh = nsh;
   p.maxes = maxes;
   p.dq = static_cast<uint16_t*>(a.dq);
   p.dk = static_cast<uint16_t*>(a.dk);
@@ -692,7 +732,7 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   p.H = a.H;
   p.N = a.N;
   p.BH = a.B * a.H;
-  p.c = a.scale * kLog2e;
+  p.c = c;
   p.scale = a.scale;
   p.key_len = a.key_len;
   p.block_mask = a.block_mask;

@@ -46,14 +46,15 @@ struct BwdArgs {
 // Backward workspace, regions 256-byte aligned, in this order:
 //   D      f32 [BHN]      D_i = sum_c dO_ic O_ic
 //   shift  f32 [BHN]      lse_i * log2(e), +inf for rows without keys
-//   Ds     f32 [BHN]      D_i * 2^-(eo+ev)          (bf16 inputs)
-//   maxes  u32 [4][BH]    max |Q|, |K|, |V|, |dO| per (b, h), float bits (bf16 inputs)
-//   q16    f16 [BHN d]    Q * 2^-eq                 (bf16 inputs)
-//   do16   f16 [BHN d]    dO * 2^-eo                (bf16 inputs)
-// (BHN = B*H*N; eq, eo, ev are the per-(b, h) power-of-two exponents that
-// the kernels derive from the maxima.)
+//   nDs    f32 [BHN]      -D_i * 2^-(eo+ev)
+//   nsh    f32 [BHN]      -shift_i * 2^-f
+//   maxes  u32 [4][BH]    max |Q|, |K|, |V|, |dO| per (b, h), float bits
+//   q16    f16 [BHN d]    c Q * 2^-eq    (c = scale * log2(e))
+//   do16   f16 [BHN d]    dO * 2^-eo
+// (BHN = B*H*N; eq, ek, ev, eo and f = eq + ek are the per-(b, h)
+// power-of-two exponents that the kernels derive from the maxima.)
 struct BwdWorkspace {
-  size_t D, shift, Ds, maxes, q16, do16, total;
+  size_t D, shift, nDs, nsh, maxes, q16, do16, total;
 };
 
 inline size_t ws_align(size_t x) { return (x + 255) & ~size_t(255); }
@@ -63,8 +64,9 @@ inline BwdWorkspace bwd_workspace_layout(int64_t B, int64_t H, int64_t N, int64_
   BwdWorkspace w;
   w.D = 0;
   w.shift = ws_align(w.D + 4 * bhn);
-  w.Ds = ws_align(w.shift + 4 * bhn);
-  w.maxes = ws_align(w.Ds + 4 * bhn);
+  w.nDs = ws_align(w.shift + 4 * bhn);
+  w.nsh = ws_align(w.nDs + 4 * bhn);
+  w.maxes = ws_align(w.nsh + 4 * bhn);
   w.q16 = ws_align(w.maxes + 16 * bh);
   w.do16 = ws_align(w.q16 + 2 * bhn * size_t(d));
   w.total = ws_align(w.do16 + 2 * bhn * size_t(d));
