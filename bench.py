@@ -68,6 +68,64 @@ def measured_traffic(kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
+KERNEL_KEYS = (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"),
+               ("bwd_pre_kernel", "bwd_pre"), ("bwd_zero_kernel", "bwd_pre"),
+               ("bwd_convert_kernel", "bwd_pre"), ("fwd_kernel", "fwd"))
+
+
+def kernel_key(name: str):
+    for sub, key in KERNEL_KEYS:
+        if sub in name:
+            return key
+    return None
+
+
+def read_counter_csv(path: str, counter: str):
+    """{kernel name: [per-dispatch values]} of one rocprofv3 --pmc csv."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, out):
+    """HBM bytes per launch of each attention kernel from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for a plain device copy of copy_bytes bytes.  Writes
+    ``out`` (JSON) tagged with the hash of the kernel sources."""
+    def copy_factor(path, counter):
+        vals = [v for name, vs in read_counter_csv(path, counter).items()
+                if "copyBuffer" in name for v in vs]
+        return copy_bytes / (sum(vals) / len(vals) * 1024.0)
+    f_fetch = copy_factor(copy_fetch_csv, "FETCH_SIZE")
+    f_write = copy_factor(copy_write_csv, "WRITE_SIZE")
+    per = {}
+    for path, counter, fac, field in ((fetch_csv, "FETCH_SIZE", f_fetch, "fetch_bytes"),
+                                      (write_csv, "WRITE_SIZE", f_write, "write_bytes")):
+        for name, vals in read_counter_csv(path, counter).items():
+            key = kernel_key(name)
+            if key is None:
+                continue
+            # kernels of one key (the three launches of the D pass) add up
+            per.setdefault(key, {}).setdefault(field, {})[name] = sum(vals) / len(vals) * 1024 * fac
+    kernels = {}
+    for key, d in per.items():
+        fb = sum(d.get("fetch_bytes", {}).values())
+        wb = sum(d.get("write_bytes", {}).values())
+        kernels[key] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                        "bytes_per_launch": round(fb + wb)}
+    res = {"source_hash": source_hash(),
+           "calibration": {"copy_bytes": copy_bytes, "fetch_factor": round(f_fetch, 4),
+                           "write_factor": round(f_write, 4)},
+           "kernels": kernels}
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
 def cpu_baseline(x, w, budget_s=10.0, prefix=8192):
     """The fp64 oracle (forward + backward) on a bounded sample of the same
     workload: whole heads of the causal prefix of ``prefix`` tokens (a causal
@@ -105,10 +163,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV",
+                    "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_MIB"),
+                    help="write profiles/hbm_traffic.json from rocprofv3 --pmc csv files and exit")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, --steps "
                          "times (the known-size kernel that scales the HBM byte counters)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        fc, wc, cfc, cwc, mib = args.summarize_counters
+        print(json.dumps(summarize_counters(fc, wc, cfc, cwc, int(mib) << 20, TRAFFIC_FILE)))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the per-head kernels on a single "
               "MI355X; --gpus above 1 is not supported", file=sys.stderr)

@@ -82,18 +82,23 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal,
            const int32_t* key_len, int dtype, void* stream);
 
-/* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need: 8*B*H*N
- * (two floats per query row: D_i = sum_c dO_ic O_ic and the base-2 softmax
- * shift lse_i * log2(e), +inf for rows without keys).  Linear in N: the
- * method's memory grows linearly, not quadratically, in sequence length
- * ([ODP "Why it mattered"]).  Returns 0 for invalid sizes. */
+/* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need, about
+ * 16*B*H*N + 6*B*H*N*d + 16*B*H (each region rounded up to 256 bytes):
+ * per query row, D_i = sum_c dO_ic O_ic, the base-2 softmax shift
+ * lse_i * log2(e) (+inf for rows without keys) and their power-of-two
+ * scaled negations (four floats), and 16-bit copies of the row's q, k and
+ * dO scaled by powers of two; per (b, h), the maxima of |q|, |k|, |v|,
+ * |dO| that choose those powers.  Linear in N: the method's memory grows
+ * linearly, not quadratically, in sequence length ([ODP "Why it
+ * mattered"]).  Returns 0 for invalid sizes. */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
 /* Backward with recomputation ([ODP "The key idea"]; [DEC "The Hardware
  * Picture: Why Tiling Wins"]): the probabilities are rebuilt on-chip from
- * q, k and lse; nothing of size N x N is stored.  Three launches on
- * `stream`: D = rowsum(dO * O); dK/dV (one workgroup per key tile);
- * dQ (one workgroup per query tile).  Deterministic (no atomics).
+ * q, k and lse; nothing of size N x N is stored.  Launches on `stream`:
+ * D = rowsum(dO * O) with the operand copies; dK/dV (one workgroup per key tile);
+ * dQ (one workgroup per query tile).  Deterministic: the only atomics take
+ * maxima, whose result does not depend on order.
  *   o, lse  : the forward's outputs for the same inputs and mask
  *   dO      : upstream gradient [B][H][N][d], dtype
  *   dq,dk,dv: outputs [B][H][N][d], dtype (overwritten)
@@ -123,11 +128,13 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v,
                        int block_size, void* workspace, size_t workspace_bytes,
                        int dtype, void* stream);
 
-/* The three launches of fa_bwd / fa_bwd_blocksparse, one at a time, for
+/* The three stages of fa_bwd / fa_bwd_blocksparse, one at a time, for
  * callers that schedule them separately (to time each kernel, or to place
  * them on different streams with their own events).
- *   stage FA_BWD_STAGE_D    : workspace[i] = D_i = sum_c dO_ic O_ic and
- *                             workspace[B*H*N + i] = lse_i * log2(e)
+ *   stage FA_BWD_STAGE_D    : the workspace: D_i = sum_c dO_ic O_ic, the
+ *                             softmax shift, the per-(b, h) maxima and the
+ *                             scaled 16-bit copies of q, k and dO
+ *                             (three launches)
  *   stage FA_BWD_STAGE_DKDV : dk, dv (reads the workspace written by stage 1)
  *   stage FA_BWD_STAGE_DQ   : dq     (reads the workspace written by stage 1)
  * Running stages 1, 2, 3 in this order on one stream equals fa_bwd.  The

@@ -213,16 +213,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
   }
 }
 
-// c Q * 2^-eq and dO * 2^-eo as fp16; -shift * 2^-f and -D * 2^-(eo+ev)
+// c Q * 2^-eq, K * 2^-ek and dO * 2^-eo as fp16; -shift * 2^-f and -D * 2^-(eo+ev)
 // per row (the initial values of the dK/dV kernel's score and dP
 // accumulators).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, const uint16_t* dO,
-                                                          const float* Dbuf, const float* shift,
+__global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, const uint16_t* k,
+                                                          const uint16_t* dO, const float* Dbuf,
+                                                          const float* shift,
                                                           const uint32_t* maxes, float c,
-                                                          uint16_t* q16, uint16_t* do16,
-                                                          float* nDs, float* nsh, int64_t rows,
-                                                          int N, int BH) {
+                                                          uint16_t* q16, uint16_t* k16,
+                                                          uint16_t* do16, float* nDs, float* nsh,
+                                                          int64_t rows, int N, int BH) {
   constexpr int TPR = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid / TPR;
@@ -232,15 +233,19 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, con
   const float cq = ldexpf(c, -sc.eq);
   const u32x4 a = *reinterpret_cast<const u32x4*>(q + row * D + col);
   const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + col);
-  u32x4 ra, rg;
+  const u32x4 kk = *reinterpret_cast<const u32x4*>(k + row * D + col);
+  u32x4 ra, rg, rk;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     ra[j] = Elt<_Float16>::pack2(cq * to_f32<T>(a[j] & 0xffffu), cq * to_f32<T>(a[j] >> 16));
     rg[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(g[j] & 0xffffu), -sc.eo),
                                  ldexpf(to_f32<T>(g[j] >> 16), -sc.eo));
+    rk[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(kk[j] & 0xffffu), -sc.ek),
+                                 ldexpf(to_f32<T>(kk[j] >> 16), -sc.ek));
   }
   *reinterpret_cast<u32x4*>(q16 + row * D + col) = ra;
   *reinterpret_cast<u32x4*>(do16 + row * D + col) = rg;
+  *reinterpret_cast<u32x4*>(k16 + row * D + col) = rk;
   if (col == 0) {
     nDs[row] = -ldexpf(Dbuf[row], -(sc.eo + sc.ev));
     nsh[row] = -ldexpf(shift[row], -sc.f);
@@ -257,6 +262,7 @@ struct BwdParams {
   // dK/dV kernel: fp16 copies, negated scaled D and shift, the maxima
   const uint16_t* q16;
   const uint16_t* do16;
+  const uint16_t* k16;
   const float* nDs;
   const float* nsh;
   const uint32_t* maxes;
@@ -270,6 +276,18 @@ struct BwdParams {
   const uint8_t* block_mask;
   int nblk;
 };
+
+// x as hi + mid + lo bf16 parts (24 significant bits); non-finite x goes
+// entirely into hi.
+__device__ __forceinline__ void split3_bf16(float x, __bf16 out[3]) {
+  const __bf16 hi = (__bf16)x;
+  const bool fin = __builtin_isfinite(x);
+  const float r1 = fin ? x - (float)hi : 0.f;
+  const __bf16 mid = (__bf16)r1;
+  out[0] = hi;
+  out[1] = mid;
+  out[2] = (__bf16)(r1 - (float)mid);
+}
 
 // B operand (P or dS, 16 keys or queries of chunk a) from a 32x32
 // accumulator: chunk a covers accumulator elements 8(a%2) .. 8(a%2)+7 of
@@ -510,10 +528,19 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per 128 queries, 32 per wave
+//
+// Scores run on fp16 operands (c Q 2^-eq against K 2^-ek, the fp16 copies
+// of the convert pass) and dP on the input type.  Each product gets one
+// more k-step whose A operand is a constant column of ones and whose B
+// operand carries the query's -shift 2^-f (scores) or -D (dP) split into
+// three bf16 parts, so the accumulators end as the exponent of P and as
+// dP - D: P is one exponential and dS one multiply.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32, TILE = kBC * D, NW = 4;
+  typedef _Float16 TI;
+  typedef typename Elt<TI>::vec8 hvec8;
   typedef typename Elt<T>::vec8 vec8;
   __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
@@ -529,22 +556,40 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
   const int qt = CAUSAL ? p.ntiles - 1 - rank : rank;  // longest rows first
   const int b = bh / p.H, N = p.N;
   const size_t base = (size_t)bh * N * D;
-  const uint16_t* K = p.k + base;
+  const uint16_t* K = p.k16 + base;  // K 2^-ek, fp16
   const uint16_t* V = p.v + base;
   const int L = valid_keys(p.key_len, b, N);
   const int q0 = qt * kBR, qw = q0 + wave * 32, query = qw + l32;
-  const float c = p.c;
+  const Scales sc = bwd_scales(p.maxes, p.BH, bh, p.c);
 
-  // this wave's queries and output gradients as B operands (lane = query)
-  vec8 qf[KS], of[KS];
+  // this wave's queries (c Q 2^-eq, fp16) and output gradients as B
+  // operands (lane = query, k = d values)
+  hvec8 qf[KS];
+  vec8 of[KS];
   const bool qok = query < N;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = as_vec8<T>(ldg16(p.q + base + (size_t)query * D + ks * 16 + h * 8, qok));
+    qf[ks] = as_vec8<TI>(ldg16(p.q16 + base + (size_t)query * D + ks * 16 + h * 8, qok));
     of[ks] = as_vec8<T>(ldg16(p.dO + base + (size_t)query * D + ks * 16 + h * 8, qok));
   }
-  const float sh = qok ? p.shift[(size_t)bh * N + query] : pos_inf();
-  const float dd = qok ? p.Dbuf[(size_t)bh * N + query] : 0.f;
+  // the extra k-step (a bf16 MFMA into the same fp32 accumulators, so any
+  // magnitude fits): A = 1 in k-slots 0..2 (lanes h = 0), B = the row value
+  // split into three bf16 parts there (24 significant bits), zero elsewhere
+  bf16x8 one_b, s_aug_b, d_aug_b;
+  {
+    const float ns = qok ? p.nsh[(size_t)bh * N + query] : neg_inf();
+    const float nd = qok ? -p.Dbuf[(size_t)bh * N + query] : 0.f;
+    __bf16 sp[3], dq3[3];
+    split3_bf16(ns, sp);
+    split3_bf16(nd, dq3);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool slot = h == 0 && j < 3;
+      one_b[j] = slot ? (__bf16)1.f : (__bf16)0.f;
+      s_aug_b[j] = slot ? sp[j < 3 ? j : 0] : (__bf16)0.f;
+      d_aug_b[j] = slot ? dq3[j < 3 ? j : 0] : (__bf16)0.f;
+    }
+  }
   f32x16 acc[DB];  // dQ^T: rows d = 32db + 8i + 4h + j, column = query
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -563,44 +608,60 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
 
   const TileCopy<D, kBC, NW> copy(wave, lane);
 
-  auto compute = [&](const uint16_t* tk, const uint16_t* tv, int kt0) __attribute__((always_inline)) {
-    if (qw >= N) return;
-    if (CAUSAL && kt0 > qw + 31) return;  // tile above the diagonal
+  // `prefetch` starts the copies of the next tile; it runs inside the
+  // compute, after the score products are issued, so that the copies (which
+  // can stall issue while the CU's vector-memory path is busy) overlap
+  // matrix-core work instead of delaying it
+  auto compute = [&](const uint16_t* tk, const uint16_t* tv, int kt0, auto prefetch)
+      __attribute__((always_inline)) {
+    if (qw >= N || (CAUSAL && kt0 > qw + 31)) {  // no rows / tile above the diagonal
+      prefetch();
+      return;
+    }
     f32x16 s[2], dp[2];  // rows = keys 32 kb + 8i + 4h + j, column = query
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = dp[kb][e] = 0.f;
+      s[kb] = Elt<__bf16>::mfma32(one_b, s_aug_b, s[kb]);
+      dp[kb] = Elt<__bf16>::mfma32(one_b, d_aug_b, dp[kb]);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const vec8 ak = as_vec8<T>(lds16(tk + roff[ks] + kb * 32 * D));
+        const hvec8 ak = as_vec8<TI>(lds16(tk + roff[ks] + kb * 32 * D));
         const vec8 av = as_vec8<T>(lds16(tv + roff[ks] + kb * 32 * D));
-        s[kb] = Elt<T>::mfma32(ak, qf[ks], s[kb]);
+        s[kb] = Elt<TI>::mfma32(ak, qf[ks], s[kb]);
         dp[kb] = Elt<T>::mfma32(av, of[ks], dp[kb]);
       }
+    prefetch();
     const bool need_mask = (kt0 + kBC > L) || (CAUSAL && kt0 + kBC - 1 > qw);
+    if (sc.f != 0) {  // unbalanced operand scales (extreme input ranges only)
+      const float sf = ldexpf(1.f, sc.f);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] *= sf;
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float pv = fast_exp2(fmaf(s[kb][e], c, -sh));
+        float pv = fast_exp2(s[kb][e]);
         if (need_mask) {
           const int key = kt0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
           if (key >= L || (CAUSAL && key > query)) pv = 0.f;
         }
-        dp[kb][e] = pv * (dp[kb][e] - dd);
+        dp[kb][e] *= pv;
       }
-    // dQ^T += K^T dS^T, 16 keys (chunk a) per MFMA
+    // dQ^T += K^T dS^T  (k = 16 keys per MFMA; K 2^-ek)
 #pragma unroll
     for (int a = 0; a < kBC / 16; ++a) {
-      const vec8 sb = pack_chunk<T>(dp[a >> 1], a & 1);
+      const hvec8 sb = pack_chunk<TI>(dp[a >> 1], a & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const vec8 ak = join8<T>(lds_tr4(tk + toff[0][db] + a * 16 * D),
-                                 lds_tr4(tk + toff[1][db] + a * 16 * D));
-        acc[db] = Elt<T>::mfma32(ak, sb, acc[db]);
+        const hvec8 ak = join8<TI>(lds_tr4(tk + toff[0][db] + a * 16 * D),
+                                   lds_tr4(tk + toff[1][db] + a * 16 * D));
+        acc[db] = Elt<TI>::mfma32(ak, sb, acc[db]);
       }
     }
   };
@@ -613,12 +674,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
         __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
-      if (t + 1 < ntiles) {
-        const int k1 = key0(t + 1);
-        copy(K, k1, N, nk);
-        copy(V, k1, N, nv);
-      }
-      compute(ck, cv, key0(t));
+      auto prefetch = [&]() __attribute__((always_inline)) {
+        if (t + 1 < ntiles) {
+          const int k1 = key0(t + 1);
+          copy(K, k1, N, nk);
+          copy(V, k1, N, nv);
+        }
+      };
+      compute(ck, cv, key0(t), prefetch);
     };
     for (int t = 0; t < ntiles; t += 2) {
       step(t, sK0, sV0, sK1, sV1);
@@ -644,13 +707,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
     walk(nkt, [](int t) { return t * kBC; });
   }
 
-  if (qok) {
+  if (qok) {  // dQ = scale 2^ek (dS K')
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 q4 = {acc[db][4 * i] * p.scale, acc[db][4 * i + 1] * p.scale,
-                          acc[db][4 * i + 2] * p.scale, acc[db][4 * i + 3] * p.scale};
+        f32x4 q4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q4[j] = ldexpf(acc[db][4 * i + j] * p.scale, sc.ek);
         *reinterpret_cast<u32x2*>(p.dq + base + (size_t)query * D + db * 32 + 8 * i + 4 * h) =
             pack4<T>(q4);
       }
@@ -670,8 +734,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
   template __global__ void bwd_dq_kernel<T, D, false, false>(BwdParams);           \
   template __global__ void bwd_dq_kernel<T, D, false, true>(BwdParams);          \
   template __global__ void bwd_convert_kernel<T, D>(                               \
-      const uint16_t*, const uint16_t*, const float*, const float*, const uint32_t*, float, \
-      uint16_t*, uint16_t*, float*, float*, int64_t, int, int);
+      const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*,   \
+      const uint32_t*, float,                                                        \
+      uint16_t*, uint16_t*, uint16_t*, float*, float*, int64_t, int, int);
 FA_BWD_INSTANTIATE(__bf16, 64)
 FA_BWD_INSTANTIATE(__bf16, 128)
 FA_BWD_INSTANTIATE(_Float16, 64)
@@ -693,6 +758,7 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   uint32_t* maxes = reinterpret_cast<uint32_t*>(ws + w.maxes);
   uint16_t* q16 = reinterpret_cast<uint16_t*>(ws + w.q16);
   uint16_t* do16 = reinterpret_cast<uint16_t*>(ws + w.do16);
+  uint16_t* k16 = reinterpret_cast<uint16_t*>(ws + w.k16);
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   const uint16_t* dO = static_cast<const uint16_t*>(a.dO);
   if (stage == 0 || stage == 1) {
@@ -709,7 +775,8 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_convert_kernel<T, D>), dim3(row_blocks), dim3(256), 0, a.stream, q,
-                       dO, Dbuf, shift, maxes, c, q16, do16, nDs, nsh, rows, a.N, BH);
+                       static_cast<const uint16_t*>(a.k), dO, Dbuf, shift, maxes, c, q16, k16,
+                       do16, nDs, nsh, rows, a.N, BH);
     e = hipGetLastError();
     if (e != hipSuccess || stage == 1) return e;
   }
@@ -723,6 +790,7 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   p.Dbuf = Dbuf;
   p.q16 = q16;
   p.do16 = do16;
+  p.k16 = k16;
   p.nDs = nDs;
   p.nsh = nsh;
   p.maxes = maxes;

@@ -51,10 +51,11 @@ struct BwdArgs {
 //   maxes  u32 [4][BH]    max |Q|, |K|, |V|, |dO| per (b, h), float bits
 //   q16    f16 [BHN d]    c Q * 2^-eq    (c = scale * log2(e))
 //   do16   f16 [BHN d]    dO * 2^-eo
+//   k16    f16 [BHN d]    K * 2^-ek
 // (BHN = B*H*N; eq, ek, ev, eo and f = eq + ek are the per-(b, h)
 // power-of-two exponents that the kernels derive from the maxima.)
 struct BwdWorkspace {
-  size_t D, shift, nDs, nsh, maxes, q16, do16, total;
+  size_t D, shift, nDs, nsh, maxes, q16, do16, k16, total;
 };
 
 inline size_t ws_align(size_t x) { return (x + 255) & ~size_t(255); }
@@ -69,7 +70,8 @@ inline BwdWorkspace bwd_workspace_layout(int64_t B, int64_t H, int64_t N, int64_
   w.maxes = ws_align(w.nsh + 4 * bhn);
   w.q16 = ws_align(w.maxes + 16 * bh);
   w.do16 = ws_align(w.q16 + 2 * bhn * size_t(d));
-  w.total = ws_align(w.do16 + 2 * bhn * size_t(d));
+  w.k16 = ws_align(w.do16 + 2 * bhn * size_t(d));
+  w.total = ws_align(w.k16 + 2 * bhn * size_t(d));
   return w;
 }
 
