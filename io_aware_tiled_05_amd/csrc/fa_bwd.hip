@@ -13,11 +13,14 @@
 // D_i = sum_c dO_ic O_ic (= sum_j P_ij dP_ij), dQ = scale dS K,
 // dK = scale dS^T Q.
 //
-// Three launches, no atomics (deterministic):
+// Stages (deterministic: the only atomics take per-head maxima):
 //   bwd_pre   per query row: D and the base-2 softmax shift lse*log2(e)
-//             (+inf for rows without keys), into the workspace;
+//             (+inf for rows without keys), into the workspace, and the
+//             per-(b, h) maxima of |Q|, |K|, |V|, |dO| (bwd_zero clears
+//             them first); bwd_convert then writes the scaled fp16 copies
+//             of Q, K, dO and the scaled row terms described below;
 //   bwd_dkdv  one workgroup per 128 keys (32 per wave); query tiles of 64
-//             rows (Q, dO, shift, D) are double buffered in LDS.  With
+//             rows (Q, dO, row terms) are double buffered in LDS.  With
 //             v_mfma_f32_32x32x16, S = Q K^T and dP = dO V^T come out with
 //             the key in the lane's column, so P and dS rounded to 16 bits
 //             are directly the k-operands of dV^T += dO^T P and
@@ -29,7 +32,7 @@
 // LDS tiles are XOR-swizzled (conflict-free row and transpose reads) and
 // filled by direct global->LDS copies one tile ahead of the compute.
 //
-// The dK/dV products run on fp16 operands for both input types.  Rounding
+// The products run on fp16 operands for both input types.  Rounding
 // P and dS to bf16 (8 significant bits) before dV = P^T dO and dK = dS^T Q
 // costs up to ~0.01 absolute in the gradients, next to the output
 // rounding; fp16 keeps 11 bits.  The D pass also finds max |Q|, |K|, |V|,
