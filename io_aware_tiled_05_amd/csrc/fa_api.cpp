@@ -78,6 +78,21 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
 
 }  // namespace
 
+namespace fa {
+
+int device_cu_count() {
+  static int cached[64];  // per device id; 0 = not queried yet (benign race: same value)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  if (dev < 64 && n > 0) cached[dev] = n;
+  return n;
+}
+
+}  // namespace fa
+
 extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

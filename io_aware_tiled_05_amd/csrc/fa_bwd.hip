@@ -54,6 +54,10 @@ namespace fa {
 
 namespace bwd {
 
+#ifndef FA_BWD_SNAKE
+#define FA_BWD_SNAKE 0  // snake workgroup order in the causal dK/dV and dQ kernels
+#endif
+
 constexpr int kBKV = 128;      // keys per dK/dV workgroup (= block-sparse block)
 constexpr int kBQ = 64;        // query rows per LDS tile in the dK/dV kernel
 constexpr int kBR = 128;       // queries per dQ workgroup (= block-sparse block)
@@ -273,6 +277,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   int H, N, BH, ntiles;
+  int period;  // snake period of map_workgroup (0: plain order)
   float c;      // scale * log2(e)
   float scale;
   const int32_t* key_len;
@@ -352,7 +357,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5, sub = lane & 15, g4 = lane >> 4;
   int rank, bh;
-  map_workgroup(blockIdx.x, p.ntiles, p.BH, &rank, &bh);
+  map_workgroup(blockIdx.x, p.ntiles, p.BH, p.period, &rank, &bh);
   const int kt = rank;  // causal: the lowest key tiles see the most queries, so go first
   const int b = bh / p.H, N = p.N;
   const size_t base = (size_t)bh * N * D;
@@ -555,7 +560,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5, sub = lane & 15, g4 = lane >> 4;
   int rank, bh;
-  map_workgroup(blockIdx.x, p.ntiles, p.BH, &rank, &bh);
+  map_workgroup(blockIdx.x, p.ntiles, p.BH, p.period, &rank, &bh);
   const int qt = CAUSAL ? p.ntiles - 1 - rank : rank;  // longest rows first
   const int b = bh / p.H, N = p.N;
   const size_t base = (size_t)bh * N * D;
@@ -808,6 +813,7 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   p.key_len = a.key_len;
   p.block_mask = a.block_mask;
   p.nblk = (a.N + 127) / 128;
+  p.period = (FA_BWD_SNAKE && CAUSAL) ? snake_period(p.BH) : 0;
 
   if (stage == 0 || stage == 2) {
     p.ntiles = (a.N + kBKV - 1) / kBKV;

@@ -241,17 +241,37 @@ __device__ __forceinline__ float pos_inf() { return __builtin_huge_valf(); }
 // multiple of 8 every tile of one head is placed on the same XCD so that the
 // head's K/V (or Q/dO) stream is shared through that XCD's L2.  Tile rank 0
 // is dispatched first.
-__device__ __forceinline__ void map_workgroup(int id, int ntiles, int nheads,
+//
+// `period` > 0 is the number of compute units that take one workgroup each
+// per dispatch round (per XCD when heads are grouped by XCD): a CU receives
+// the workgroups period apart, so with ranks in plain order one CU gets the
+// longest tile of every round.  Reversing the order in every other round
+// ("snake") gives each CU a long and a short tile in turn, which balances
+// causal work whose length falls with the rank.
+// Reverses slot order inside every odd round of `period` slots; a partial
+// last round is reversed within its own length, so the map is a permutation
+// of [0, total).
+__host__ __device__ inline int snake(int slot, int period, int total) {
+  if (period <= 0) return slot;
+  const int round = slot / period, pos = slot - round * period, first = round * period;
+  if ((round & 1) == 0) return slot;
+  const int len = total - first < period ? total - first : period;
+  return first + (len - 1 - pos);
+}
+
+// ntiles tiles per head, nheads heads, grid = ntiles * nheads workgroups.
+__host__ __device__ inline void map_workgroup(int id, int ntiles, int nheads, int period,
                                               int* rank, int* head) {
   if ((nheads & 7) == 0) {
-    const int xcd = id & 7, slot = id >> 3, hpx = nheads >> 3;
+    const int xcd = id & 7, hpx = nheads >> 3;
+    const int slot = snake(id >> 3, period, ntiles * hpx);
     *rank = slot / hpx;
     *head = xcd + 8 * (slot % hpx);
   } else {
-    *rank = id / nheads;
-    *head = id % nheads;
+    const int slot = snake(id, period, ntiles * nheads);
+    *rank = slot / nheads;
+    *head = slot % nheads;
   }
-  (void)ntiles;
 }
 
 }  // namespace fa

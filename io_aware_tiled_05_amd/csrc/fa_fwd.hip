@@ -43,6 +43,7 @@ struct FwdParams {
   uint16_t* o;
   float* lse;
   int H, N, BH, nqt;
+  int period;  // snake period of map_workgroup (0: plain order)
   float c;  // scale * log2(e)
   const int32_t* key_len;
   const uint8_t* block_mask;
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(Fwd
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   int rank, bh;
-  map_workgroup(blockIdx.x, p.nqt, p.BH, &rank, &bh);
+  map_workgroup(blockIdx.x, p.nqt, p.BH, p.period, &rank, &bh);
   const int qt = CAUSAL ? p.nqt - 1 - rank : rank;  // longest rows first
   const int b = bh / p.H, N = p.N;
   const size_t base = (size_t)bh * N * D;
@@ -333,6 +334,7 @@ struct FwdParamsF32 {
   float* o;
   float* lse;
   int H, N, BH, nqt;
+  int period;
   float c;
   const int32_t* key_len;
 };
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParamsF32 p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   int rank, bh;
-  map_workgroup(blockIdx.x, p.nqt, p.BH, &rank, &bh);
+  map_workgroup(blockIdx.x, p.nqt, p.BH, p.period, &rank, &bh);
   const int qt = CAUSAL ? p.nqt - 1 - rank : rank;
   const int b = bh / p.H, N = p.N;
   const size_t base = (size_t)bh * N * D;
@@ -501,6 +503,7 @@ hipError_t run_fwd(const FwdArgs& a) {
   p.N = a.N;
   p.BH = a.B * a.H;
   p.nqt = (a.N + BR - 1) / BR;
+  p.period = CAUSAL ? snake_period(p.BH) : 0;
   p.c = a.scale * kLog2e;
   p.key_len = a.key_len;
   p.block_mask = a.block_mask;
@@ -522,6 +525,7 @@ hipError_t run_fwd_f32(const FwdArgs& a) {
   p.N = a.N;
   p.BH = a.B * a.H;
   p.nqt = (a.N + kBR - 1) / kBR;
+  p.period = CAUSAL ? snake_period(p.BH) : 0;
   p.c = a.scale * kLog2e;
   p.key_len = a.key_len;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(p.nqt * p.BH), dim3(256), 0, a.stream, p);

@@ -75,6 +75,16 @@ inline BwdWorkspace bwd_workspace_layout(int64_t B, int64_t H, int64_t N, int64_
   return w;
 }
 
+// Compute units of the current device (0 if the query fails); cached.
+int device_cu_count();
+
+// Dispatch-round length for map_workgroup's snake order: CUs per XCD when
+// the heads are grouped by XCD (head count a multiple of 8), else all CUs.
+inline int snake_period(int nheads) {
+  const int n = device_cu_count();
+  return (nheads & 7) == 0 ? n / 8 : n;
+}
+
 hipError_t launch_fwd(const FwdArgs& a);
 // stage 0: all three launches; 1: D only; 2: dK/dV only; 3: dQ only
 hipError_t launch_bwd(const BwdArgs& a, int stage);
