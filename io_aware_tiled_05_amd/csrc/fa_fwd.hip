@@ -97,230 +97,239 @@ __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(Fwd
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   int rank, bh;
-  map_workgroup(blockIdx.x, p.nqt, p.BH, p.period, &rank, &bh);
-  const int qt = CAUSAL ? p.nqt - 1 - rank : rank;  // longest rows first
-  const int b = bh / p.H, N = p.N;
-  const size_t base = (size_t)bh * N * D;
-  const uint16_t* Q = p.q + base;
-  const uint16_t* K = p.k + base;
-  const uint16_t* V = p.v + base;
-  const int L = valid_keys(p.key_len, b, N);
-  const int q0 = qt * BR, qw = q0 + wave * QW;
-  const float c = p.c;
+  // Dense causal: a workgroup takes the query tiles nqt-1-r and r of one
+  // head in turn, so every workgroup sees the same number of key tiles and
+  // all of them end together; otherwise a workgroup takes one tile.
+  constexpr bool kPairs = CAUSAL && !SPARSE;
+  map_workgroup(blockIdx.x, kPairs ? (p.nqt + 1) / 2 : p.nqt, p.BH, p.period, &rank, &bh);
+  const int npass = kPairs && p.nqt - 1 - rank != rank ? 2 : 1;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int qt = CAUSAL ? (pass == 0 ? p.nqt - 1 - rank : rank) : rank;
+    const int b = bh / p.H, N = p.N;
+    const size_t base = (size_t)bh * N * D;
+    const uint16_t* Q = p.q + base;
+    const uint16_t* K = p.k + base;
+    const uint16_t* V = p.v + base;
+    const int L = valid_keys(p.key_len, b, N);
+    const int q0 = qt * BR, qw = q0 + wave * QW;
+    const float c = p.c;
 
-  // This wave's queries as B operands of S^T = K Q^T: lane = query column
-  // l32 of block qb, k = d values 16 ks + 8 h .. +7.
-  vec8 qf[NQB][KS];
+    // This wave's queries as B operands of S^T = K Q^T: lane = query column
+    // l32 of block qb, k = d values 16 ks + 8 h .. +7.
+    vec8 qf[NQB][KS];
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int row = qw + qb * 32 + l32;
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int row = qw + qb * 32 + l32;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[qb][ks] = as_vec8<T>(ldg16(Q + (size_t)row * D + ks * 16 + h * 8, row < N));
-  }
+      for (int ks = 0; ks < KS; ++ks)
+        qf[qb][ks] = as_vec8<T>(ldg16(Q + (size_t)row * D + ks * 16 + h * 8, row < N));
+    }
 
-  float m[NQB], mc[NQB], l[NQB];  // reference max (raw score), m * c, partial row sum
-  f32x16 acc[DB][NQB];            // O^T, relative to the reference
+    float m[NQB], mc[NQB], l[NQB];  // reference max (raw score), m * c, partial row sum
+    f32x16 acc[DB][NQB];            // O^T, relative to the reference
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    m[qb] = neg_inf();
-    mc[qb] = neg_inf();  // "no reference yet": forces the rescaling path
-    l[qb] = 0.f;
+    for (int qb = 0; qb < NQB; ++qb) {
+      m[qb] = neg_inf();
+      mc[qb] = neg_inf();  // "no reference yet": forces the rescaling path
+      l[qb] = 0.f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[db][qb][e] = 0.f;
-  }
+        for (int e = 0; e < 16; ++e) acc[db][qb][e] = 0.f;
+    }
 
-  // per-lane LDS element offsets (tile-invariant)
-  // K reads: row kb*32 + l32, chunk 2 ks + h  -> kb adds 32*D
-  int koff[KS];
+    // per-lane LDS element offsets (tile-invariant)
+    // K reads: row kb*32 + l32, chunk 2 ks + h  -> kb adds 32*D
+    int koff[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = tile_off<D>(l32, ks * 16 + h * 8);
-  // V^T transpose reads: 16-lane group g4 = lane / 16; lanes of a group
-  // address rows 16a + 4h + sub/4 (+8 for the second read), columns
-  // db*32 + 16*(g4&1) + 4*(sub%4) .. +3.  a adds 16*D.
-  const int sub = lane & 15, g4 = lane >> 4;
-  int voff[2][DB];
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = tile_off<D>(l32, ks * 16 + h * 8);
+    // V^T transpose reads: 16-lane group g4 = lane / 16; lanes of a group
+    // address rows 16a + 4h + sub/4 (+8 for the second read), columns
+    // db*32 + 16*(g4&1) + 4*(sub%4) .. +3.  a adds 16*D.
+    const int sub = lane & 15, g4 = lane >> 4;
+    int voff[2][DB];
 #pragma unroll
-  for (int sec = 0; sec < 2; ++sec)
+    for (int sec = 0; sec < 2; ++sec)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      voff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec, db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
+      for (int db = 0; db < DB; ++db)
+        voff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec,
+                                    db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
 
-  // one 64-key tile from LDS buffer `buf` (key rows kt0 ..)
-  auto compute = [&](const uint16_t* kt, const uint16_t* vt, int kt0) {
-    if (qw >= N) return;                        // wave has no query rows
-    if (CAUSAL && kt0 > qw + QW - 1) return;    // tile above the diagonal
+    // one 64-key tile from LDS buffer `buf` (key rows kt0 ..)
+    auto compute = [&](const uint16_t* kt, const uint16_t* vt, int kt0) {
+      if (qw >= N) return;                        // wave has no query rows
+      if (CAUSAL && kt0 > qw + QW - 1) return;    // tile above the diagonal
 
-    // S^T for 64 keys (2 blocks of 32) x QW queries
-    f32x16 s[2][NQB];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[kb][qb][e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const vec8 a = as_vec8<T>(lds16(kt + koff[ks] + kb * 32 * D));
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = Elt<T>::mfma32(a, qf[qb][ks], s[kb][qb]);
-      }
-
-    // -inf on keys past key_len / above the diagonal (boundary tiles only);
-    // accumulator element 4i+j of block kb is key kt0 + 32kb + 8i + 4h + j
-    const bool need_mask = (kt0 + kBC > L) || (CAUSAL && kt0 + kBC - 1 > qw);
-    if (need_mask) {
+      // S^T for 64 keys (2 blocks of 32) x QW queries
+      f32x16 s[2][NQB];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = kt0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-            const int query = qw + qb * 32 + l32;
-            if (key >= L || (CAUSAL && key > query)) s[kb][qb][e] = neg_inf();
-          }
-    }
-
-    // P = exp2(c s - m c), packed to 16 bits; rs = this lane's part of the
-    // tile's row sum (of the rounded values)
-    uint32_t pk[2][NQB][8];
-    float rs[NQB];
-    auto exp_pack = [&](int qb, float msc) {
-      float r[4] = {0.f, 0.f, 0.f, 0.f};  // four independent sum chains
+          for (int e = 0; e < 16; ++e) s[kb][qb][e] = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x0 = fast_exp2(fmaf(s[kb][qb][2 * e], c, -msc));
-          const float x1 = fast_exp2(fmaf(s[kb][qb][2 * e + 1], c, -msc));
-          pk[kb][qb][e] = Elt<T>::pack2(x0, x1);
-          r[e & 3] = Elt<T>::sum2(pk[kb][qb][e], r[e & 3]);
+        for (int kb = 0; kb < 2; ++kb) {
+          const vec8 a = as_vec8<T>(lds16(kt + koff[ks] + kb * 32 * D));
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = Elt<T>::mfma32(a, qf[qb][ks], s[kb][qb]);
         }
-      rs[qb] = (r[0] + r[1]) + (r[2] + r[3]);
-    };
-    bool over = false;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      exp_pack(qb, mc[qb]);
-      over |= !(rs[qb] <= kRescaleAt);
-    }
-    if (__builtin_amdgcn_ballot_w64(over) != 0) {
-      // move the reference to the running maximum and rescale
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float mx = s[0][qb][0];
+
+      // -inf on keys past key_len / above the diagonal (boundary tiles only);
+      // accumulator element 4i+j of block kb is key kt0 + 32kb + 8i + 4h + j
+      const bool need_mask = (kt0 + kBC > L) || (CAUSAL && kt0 + kBC - 1 > qw);
+      if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m[qb], mx);
-        const float msc = mn == neg_inf() ? 0.f : mn * c;
-        const float alpha = fast_exp2(m[qb] * c - msc);  // 0 while m = -inf
-        m[qb] = mn;
-        mc[qb] = mn == neg_inf() ? neg_inf() : msc;
-        l[qb] *= alpha;
+          for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
-        exp_pack(qb, msc);
+            for (int e = 0; e < 16; ++e) {
+              const int key = kt0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+              const int query = qw + qb * 32 + l32;
+              if (key >= L || (CAUSAL && key > query)) s[kb][qb][e] = neg_inf();
+            }
       }
-    }
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) l[qb] += rs[qb];
 
-    // O^T += V^T P^T, 16 keys per MFMA k-step (a = 16-key chunk of the tile)
+      // P = exp2(c s - m c), packed to 16 bits; rs = this lane's part of the
+      // tile's row sum (of the rounded values)
+      uint32_t pk[2][NQB][8];
+      float rs[NQB];
+      auto exp_pack = [&](int qb, float msc) {
+        float r[4] = {0.f, 0.f, 0.f, 0.f};  // four independent sum chains
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const vec8 va = join8<T>(lds_tr4(vt + voff[0][db] + a * 16 * D),
-                                 lds_tr4(vt + voff[1][db] + a * 16 * D));
+          for (int e = 0; e < 8; ++e) {
+            const float x0 = fast_exp2(fmaf(s[kb][qb][2 * e], c, -msc));
+            const float x1 = fast_exp2(fmaf(s[kb][qb][2 * e + 1], c, -msc));
+            pk[kb][qb][e] = Elt<T>::pack2(x0, x1);
+            r[e & 3] = Elt<T>::sum2(pk[kb][qb][e], r[e & 3]);
+          }
+        rs[qb] = (r[0] + r[1]) + (r[2] + r[3]);
+      };
+      bool over = false;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        exp_pack(qb, mc[qb]);
+        over |= !(rs[qb] <= kRescaleAt);
+      }
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+        // move the reference to the running maximum and rescale
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-          const uint32_t* pp = &pk[a >> 1][qb][(a & 1) * 4];
-          const u32x4 pb = {pp[0], pp[1], pp[2], pp[3]};
-          acc[db][qb] = Elt<T>::mfma32(va, as_vec8<T>(pb), acc[db][qb]);
+          float mx = s[0][qb][0];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float mn = fmaxf(m[qb], mx);
+          const float msc = mn == neg_inf() ? 0.f : mn * c;
+          const float alpha = fast_exp2(m[qb] * c - msc);  // 0 while m = -inf
+          m[qb] = mn;
+          mc[qb] = mn == neg_inf() ? neg_inf() : msc;
+          l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
+          exp_pack(qb, msc);
         }
       }
-    }
-  };
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) l[qb] += rs[qb];
 
-  const TileCopy<D, kBC, NW> copy(wave, lane);
-
-  // Walk `ntiles` tiles (first key of tile t = key0(t)) with the copy of
-  // tile t+1 in flight while tile t is computed.  One barrier per tile.
-  auto walk = [&](int ntiles, auto key0) {
-    if (ntiles <= 0) return;
-    copy(K, key0(0), N, sK0);
-    copy(V, key0(0), N, sV0);
-    auto step = [&](int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t landed
-      __syncthreads();                     // ... and every wave's; tile t-1 fully read
-      if (t + 1 < ntiles) {
-        const int nk = key0(t + 1);
-        copy(K, nk, N, kn);
-        copy(V, nk, N, vn);
+      // O^T += V^T P^T, 16 keys per MFMA k-step (a = 16-key chunk of the tile)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const vec8 va = join8<T>(lds_tr4(vt + voff[0][db] + a * 16 * D),
+                                   lds_tr4(vt + voff[1][db] + a * 16 * D));
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            const uint32_t* pp = &pk[a >> 1][qb][(a & 1) * 4];
+            const u32x4 pb = {pp[0], pp[1], pp[2], pp[3]};
+            acc[db][qb] = Elt<T>::mfma32(va, as_vec8<T>(pb), acc[db][qb]);
+          }
+        }
       }
-      compute(kc, vc, key0(t));
     };
-    for (int t = 0; t < ntiles; t += 2) {
-      step(t, sK0, sV0, sK1, sV1);
-      if (t + 1 < ntiles) step(t + 1, sK1, sV1, sK0, sV0);
-    }
-    __syncthreads();  // LDS free for the caller
-  };
 
-  if (SPARSE) {
-    // Active 128-key blocks of this 128-query block row, two tiles each,
-    // gathered into LDS a window of kListMax blocks at a time.
-    const uint8_t* mrow = p.block_mask + (size_t)qt * p.nblk;
-    for (int w0 = 0; w0 < p.nblk; w0 += kListMax) {
-      const int wend = w0 + kListMax < p.nblk ? w0 + kListMax : p.nblk;
-      int cnt = 0;
-      for (int j0 = w0; j0 < wend; j0 += 64) {
-        const int jb = j0 + lane;
-        const bool on = jb < wend && mrow[jb] != 0;
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
-        if (wave == 0 && on) sList[cnt + __builtin_popcountll(bal & ((1ull << lane) - 1))] = jb;
-        cnt += __builtin_popcountll(bal);
-      }
-      __syncthreads();
-      walk(2 * cnt, [&](int t) { return sList[t >> 1] * 128 + (t & 1) * kBC; });
-    }
-  } else {
-    int nkt = (L + kBC - 1) / kBC;
-    if (CAUSAL) {
-      const int last = (q0 + BR < N ? q0 + BR : N) - 1;
-      nkt = nkt < last / kBC + 1 ? nkt : last / kBC + 1;
-    }
-    walk(nkt, [](int t) { return t * kBC; });
-  }
+    const TileCopy<D, kBC, NW> copy(wave, lane);
 
-  // epilogue: O = O^T / l, lse = (m c + log2 l) ln 2
-  uint16_t* O = p.o + base;
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const float lt = l[qb] + __shfl_xor(l[qb], 32);
-    const int query = qw + qb * 32 + l32;
-    if (query < N) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 o4 = {acc[db][qb][4 * i] * inv, acc[db][qb][4 * i + 1] * inv,
-                            acc[db][qb][4 * i + 2] * inv, acc[db][qb][4 * i + 3] * inv};
-          *reinterpret_cast<u32x2*>(O + (size_t)query * D + db * 32 + 8 * i + 4 * h) = pack4<T>(o4);
+    // Walk `ntiles` tiles (first key of tile t = key0(t)) with the copy of
+    // tile t+1 in flight while tile t is computed.  One barrier per tile.
+    auto walk = [&](int ntiles, auto key0) {
+      if (ntiles <= 0) return;
+      copy(K, key0(0), N, sK0);
+      copy(V, key0(0), N, sV0);
+      auto step = [&](int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t landed
+        __syncthreads();                     // ... and every wave's; tile t-1 fully read
+        if (t + 1 < ntiles) {
+          const int nk = key0(t + 1);
+          copy(K, nk, N, kn);
+          copy(V, nk, N, vn);
         }
-      if (h == 0)
-        p.lse[(size_t)bh * N + query] = lt > 0.f ? (mc[qb] + fast_log2(lt)) * kLn2 : neg_inf();
+        compute(kc, vc, key0(t));
+      };
+      for (int t = 0; t < ntiles; t += 2) {
+        step(t, sK0, sV0, sK1, sV1);
+        if (t + 1 < ntiles) step(t + 1, sK1, sV1, sK0, sV0);
+      }
+      __syncthreads();  // LDS free for the caller
+    };
+
+    if (SPARSE) {
+      // Active 128-key blocks of this 128-query block row, two tiles each,
+      // gathered into LDS a window of kListMax blocks at a time.
+      const uint8_t* mrow = p.block_mask + (size_t)qt * p.nblk;
+      for (int w0 = 0; w0 < p.nblk; w0 += kListMax) {
+        const int wend = w0 + kListMax < p.nblk ? w0 + kListMax : p.nblk;
+        int cnt = 0;
+        for (int j0 = w0; j0 < wend; j0 += 64) {
+          const int jb = j0 + lane;
+          const bool on = jb < wend && mrow[jb] != 0;
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
+          if (wave == 0 && on) sList[cnt + __builtin_popcountll(bal & ((1ull << lane) - 1))] = jb;
+          cnt += __builtin_popcountll(bal);
+        }
+        __syncthreads();
+        walk(2 * cnt, [&](int t) { return sList[t >> 1] * 128 + (t & 1) * kBC; });
+      }
+    } else {
+      int nkt = (L + kBC - 1) / kBC;
+      if (CAUSAL) {
+        const int last = (q0 + BR < N ? q0 + BR : N) - 1;
+        nkt = nkt < last / kBC + 1 ? nkt : last / kBC + 1;
+      }
+      walk(nkt, [](int t) { return t * kBC; });
     }
-  }
+
+    // epilogue: O = O^T / l, lse = (m c + log2 l) ln 2
+    uint16_t* O = p.o + base;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const float lt = l[qb] + __shfl_xor(l[qb], 32);
+      const int query = qw + qb * 32 + l32;
+      if (query < N) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 o4 = {acc[db][qb][4 * i] * inv, acc[db][qb][4 * i + 1] * inv,
+                              acc[db][qb][4 * i + 2] * inv, acc[db][qb][4 * i + 3] * inv};
+            *reinterpret_cast<u32x2*>(O + (size_t)query * D + db * 32 + 8 * i + 4 * h) =
+                pack4<T>(o4);
+          }
+        if (h == 0)
+          p.lse[(size_t)bh * N + query] = lt > 0.f ? (mc[qb] + fast_log2(lt)) * kLn2 : neg_inf();
+      }
+    }
+  }  // pass
 }
 
 // ---------------------------------------------------------------------------
@@ -503,12 +512,14 @@ hipError_t run_fwd(const FwdArgs& a) {
   p.N = a.N;
   p.BH = a.B * a.H;
   p.nqt = (a.N + BR - 1) / BR;
-  p.period = CAUSAL ? snake_period(p.BH) : 0;
+  p.period = 0;  // dense causal tiles are paired per workgroup; other tiles are uniform
   p.c = a.scale * kLog2e;
   p.key_len = a.key_len;
   p.block_mask = a.block_mask;
   p.nblk = (a.N + 127) / 128;
-  hipLaunchKernelGGL((fwd_kernel<T, D, NW, CAUSAL, SPARSE>), dim3(p.nqt * p.BH), dim3(64 * NW),
+  const int wgs_per_head = CAUSAL && !SPARSE ? (p.nqt + 1) / 2 : p.nqt;
+  hipLaunchKernelGGL((fwd_kernel<T, D, NW, CAUSAL, SPARSE>), dim3(wgs_per_head * p.BH),
+                     dim3(64 * NW),
                      0, a.stream, p);
   return hipGetLastError();
 }
