@@ -442,18 +442,33 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) s[qb] *= sf;
     }
+    // The visibility test is hoisted out of the element loop and done with
+    // selects: query q0 + 32qb + 4h + o, o = 8(e/4) + e%4, sees this lane's
+    // key iff lo <= o < hi.
+    if (need_mask) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qbase = q0 + qb * 32 + 4 * h;
+        const int hi = key < L ? N - qbase : -64;     // past N, or the key is padded
+        const int lo = CAUSAL ? key - qbase : -64;    // queries before the key
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float pv = fast_exp2(s[qb][e]);
-        if (need_mask) {
-          const int query = q0 + qb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (key >= L || query >= N || (CAUSAL && key > query)) pv = 0.f;
+        for (int e = 0; e < 16; ++e) {
+          const int o = 8 * (e >> 2) + (e & 3);
+          const float pv = ((o >= lo) & (o < hi)) ? fast_exp2(s[qb][e]) : 0.f;
+          s[qb][e] = pv;
+          dp[qb][e] *= pv;
         }
-        s[qb][e] = pv;
-        dp[qb][e] *= pv;
       }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float pv = fast_exp2(s[qb][e]);
+          s[qb][e] = pv;
+          dp[qb][e] *= pv;
+        }
+    }
     // dV^T += dO^T P, dK^T += Q^T dS, 16 queries (chunk a) per MFMA
 #pragma unroll
     for (int a = 0; a < kBQ / 16; ++a) {
@@ -650,17 +665,26 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] *= sf;
     }
+    // key kt0 + 32kb + 4h + o, o = 8(e/4) + e%4, is visible to this lane's
+    // query iff o <= thr (the test hoisted out of the element loop, selects)
+    if (need_mask) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kbase = kt0 + kb * 32 + 4 * h;
+        int thr = L - 1 - kbase;
+        if (CAUSAL) thr = min(thr, query - kbase);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float pv = fast_exp2(s[kb][e]);
-        if (need_mask) {
-          const int key = kt0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (key >= L || (CAUSAL && key > query)) pv = 0.f;
+        for (int e = 0; e < 16; ++e) {
+          const int o = 8 * (e >> 2) + (e & 3);
+          dp[kb][e] *= o <= thr ? fast_exp2(s[kb][e]) : 0.f;
         }
-        dp[kb][e] *= pv;
       }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dp[kb][e] *= fast_exp2(s[kb][e]);
+    }
     // dQ^T += K^T dS^T  (k = 16 keys per MFMA; K 2^-ek)
 #pragma unroll
     for (int a = 0; a < kBC / 16; ++a) {
