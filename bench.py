@@ -18,6 +18,13 @@ per visible (query, key) pair forward (Q K^T and P V) and 10 d backward
 
 Prints one JSON line.  The default workload is the long causal one (B=1,
 H=16, N=16384, d=64, bf16), the configuration the target is quoted on.
+
+    python bench.py --decode [--steps K] [--warmup W]
+
+instead times fa_decode (one new query per sequence against a 16384-key
+cache: B=16, H=16, d=64, bf16) and reports the rate at which it streams K
+and V, against MI355X's 8 TB/s HBM: the decode reads each cached key and
+value once and does 4 d flops per key, so it is bound by HBM, not MFMA.
 """
 
 from __future__ import annotations
@@ -156,6 +163,47 @@ def cpu_baseline(x, w, budget_s=10.0, prefix=8192):
     }
 
 
+HBM_PEAK_GBS = 8000.0
+
+
+def bench_decode(args, fa, torch, np):
+    """One JSON line: fa_decode throughput as K/V bytes streamed per second."""
+    from workloads import make_decode_inputs
+    B, H, Nq, Nk, d = 16, 16, 1, 16384, 64
+    fa.load()
+    dev = torch.device("cuda:0")
+    x = make_decode_inputs(B, H, Nq, Nk, d, "bf16", seed=5)
+    q, k, v = (torch.from_numpy(x[n]).to(dev, torch.bfloat16).contiguous() for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_decode_workspace_size(B, H, Nq, Nk, d) // 4 + 4, dtype=torch.float32,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        fa.fa_decode(q, k, v, scale=x["scale"], out=o, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        fa.fa_decode(q, k, v, scale=x["scale"], out=o, lse=lse, workspace=ws)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    kv_bytes = 2 * B * H * Nk * d * 2          # K and V, bf16, read once
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "decode attention K/V streaming rate, bf16 d=64, 1 GPU",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic N(0,1), seeded",
+        "config": {"workload": "decode_long_context", "B": B, "H": H, "Nq": Nq, "Nk": Nk,
+                   "d": d},
+        "roofline": {"kernel": "decode (partial + merge launches)", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +214,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV",
                     "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_MIB"),
                     help="write profiles/hbm_traffic.json from rocprofv3 --pmc csv files and exit")
+    ap.add_argument("--decode", action="store_true",
+                    help="time fa_decode on the long-context decode shape instead")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, --steps "
                          "times (the known-size kernel that scales the HBM byte counters)")
@@ -193,6 +243,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "steps": args.steps}))
+        return
+
+    if args.decode:
+        bench_decode(args, fa, torch, np)
         return
 
     w = WORKLOADS[args.workload]

@@ -150,6 +150,30 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v,
                  int block_size, void* workspace, size_t workspace_bytes,
                  int dtype, void* stream);
 
+/* Bytes of device workspace fa_decode needs: one partial result (d + 2
+ * floats) per (b, h, query, key chunk), the keys split into chunks of 256 to
+ * 1024 rows.  Linear in Nq and Nk.  Returns 0 for invalid sizes. */
+size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d);
+
+/* Decode: Nq new queries per (b, h) against Nk keys and values (the cached
+ * sequence, the new tokens' own keys included), O = softmax(q k^T * scale +
+ * mask) v with key j visible to every query iff j < key_len[b] (NULL: all
+ * Nk); no causal order among the Nq queries (for Nq = 1 this is causal
+ * decoding).  The same exact attention as fa_fwd ([ODP] "The key idea":
+ * running maximum and sum, partial outputs rescaled to a common maximum),
+ * split over the keys for short query blocks: one launch leaves a partial
+ * (O, m, l) per key chunk in the workspace, a second merges them.
+ *   q, o    : [B][H][Nq][d], dtype;   k, v: [B][H][Nk][d], dtype
+ *   lse     : [B][H][Nq] fp32 (natural log; -inf and O = 0 for a query
+ *             without visible keys)
+ *   workspace / workspace_bytes: device scratch >= fa_decode_workspace_size
+ * dtype FA_F32, FA_F16 or FA_BF16; d 64 or 128.  Products and the softmax
+ * run in fp32.  Errors as for fa_fwd (a small workspace is
+ * FA_ERR_INVALID). */
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Nq, int Nk, int d, float scale, const int32_t* key_len, void* workspace,
+              size_t workspace_bytes, int dtype, void* stream);
+
 /* Static description of a status code ("ok", "invalid argument", ...). */
 const char* fa_status_string(int status);
 

@@ -16,7 +16,7 @@ from ._lib import (FA_BF16, FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ, 
                    FA_F32, FA_OK, FaError, check, load)
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_fwd_blocksparse", "fa_bwd_blocksparse", "fa_bwd_stage",
-           "fa_bwd_workspace_size", "FaError", "load"]
+           "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "FaError", "load"]
 
 
 def _torch():
@@ -178,3 +178,36 @@ def fa_bwd_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, workspace, scale=None, 
                              workspace.numel() * workspace.element_size(), _dtype_code(q),
                              _stream(stream))
     check("fa_bwd_stage", st)
+
+
+def fa_decode_workspace_size(B, H, Nq, Nk, d):
+    return int(load().fa_decode_workspace_size(B, H, Nq, Nk, d))
+
+
+def fa_decode(q, k, v, scale=None, key_len=None, out=None, lse=None, workspace=None,
+              stream=None):
+    """Nq new queries [B, H, Nq, d] against keys/values [B, H, Nk, d] (keys
+    j >= key_len[b] hidden, no causal order); see include/fa.h (fa_decode).
+    Returns (O [B, H, Nq, d], lse [B, H, Nq])."""
+    torch = _torch()
+    for t in (q, k, v):
+        if t.dim() != 4 or t.dtype != q.dtype or not t.is_cuda or t.device != q.device:
+            raise ValueError("q, k, v must be [B, H, n, d] tensors of one dtype on one GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    kl = _key_len(key_len, q)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = fa_decode_workspace_size(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    st = load().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                          _scale(scale, d), _ptr(kl), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _dtype_code(q),
+                          _stream(stream))
+    check("fa_decode", st)
+    return o, lse

@@ -149,6 +149,29 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* 
                     block_mask, workspace, workspace_bytes, dtype, stream, 0);
 }
 
+size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return 0;
+  return fa::decode_split(B, H, Nq, Nk, d).ws_bytes;
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Nq, int Nk, int d, float scale, const int32_t* key_len, void* workspace,
+              size_t workspace_bytes, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(workspace))
+    return FA_ERR_INVALID;
+  int st = check_dtype(dtype);
+  if (st == FA_OK) st = check_scale(scale);
+  if (st == FA_OK) st = check_sizes(B, H, Nq, d);
+  if (st == FA_OK) st = check_sizes(B, H, Nk, d);
+  if (st != FA_OK) return st;
+  if (workspace_bytes < fa_decode_workspace_size(B, H, Nq, Nk, d)) return FA_ERR_INVALID;
+  fa::DecodeArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, scale, key_len, workspace, dtype,
+                   static_cast<hipStream_t>(stream)};
+  return hip_status(fa::launch_decode(a));
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

@@ -85,6 +85,43 @@ inline int snake_period(int nheads) {
   return (nheads & 7) == 0 ? n / 8 : n;
 }
 
+// Decode: Nq queries against Nk keys per (b, h), no causal order between
+// them; keys j >= key_len[b] hidden.  The keys are split into chunks of
+// `chunk` rows, one workgroup per (chunk, head, group of 4 queries); the
+// workspace holds one partial (O slice, m, l) per (head, query, chunk).
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Nq, Nk, d;
+  float scale;
+  const int32_t* key_len;
+  void* workspace;
+  int dtype;
+  hipStream_t stream;
+};
+
+struct DecodeSplit {
+  int chunk, nchunks;
+  size_t ws_bytes;
+};
+
+// Chunks of 1024 keys, halved (down to 256) while the launch would have
+// fewer than 1024 workgroups.
+inline DecodeSplit decode_split(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
+  const int64_t groups = B * H * ((Nq + 3) / 4);
+  int64_t chunk = 1024;
+  while (chunk > 256 && groups * ((Nk + chunk - 1) / chunk) < 1024) chunk /= 2;
+  DecodeSplit s;
+  s.chunk = (int)chunk;
+  s.nchunks = (int)((Nk + chunk - 1) / chunk);
+  s.ws_bytes = size_t(B * H * Nq) * size_t(s.nchunks) * size_t(d + 2) * sizeof(float);
+  return s;
+}
+
+hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_fwd(const FwdArgs& a);
 // stage 0: all three launches; 1: D only; 2: dK/dV only; 3: dQ only
 hipError_t launch_bwd(const BwdArgs& a, int stage);

@@ -30,8 +30,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd",
-        "fa_fwd_blocksparse", "fa_status_string"])
+        "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_decode",
+        "fa_decode_workspace_size", "fa_fwd", "fa_fwd_blocksparse", "fa_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -179,3 +179,32 @@ def stage(lib, st, **kw):
 ])
 def test_bwd_stage_validation(lib, st, kw, status):
     assert stage(lib, st, **kw) == status
+
+
+def test_decode_workspace(lib):
+    # one partial (d + 2 floats) per (b, h, query, key chunk); chunks of
+    # 256 .. 1024 keys, halved while the launch has under 1024 workgroups
+    assert lib.fa_decode_workspace_size(1, 16, 1, 16384, 64) == 16 * 64 * 66 * 4  # 256-key chunks
+    assert lib.fa_decode_workspace_size(8, 32, 1, 65536, 128) == 256 * 64 * 130 * 4  # 1024
+    assert lib.fa_decode_workspace_size(1, 1, 1, 1, 64) == 66 * 4
+    assert lib.fa_decode_workspace_size(0, 1, 1, 1, 64) == 0
+    assert lib.fa_decode_workspace_size(1, 1, 1, 0, 64) == 0
+
+
+def decode(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=1, Nk=1000, d=64, scale=0.125,
+             key_len=None, ws=P, ws_bytes=1 << 20, dtype=BF16)
+    a.update(kw)
+    return lib.fa_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                         a["Nk"], a["d"], a["scale"], a["key_len"], a["ws"], a["ws_bytes"],
+                         a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(lse=None), -1), (dict(ws=None), -1), (dict(k=P + 4), -1),
+    (dict(Nq=0), -1), (dict(Nk=0), -1), (dict(B=0), -1), (dict(d=96), -2),
+    (dict(scale=0.0), -1), (dict(dtype=9), -1), (dict(ws_bytes=16), -1),
+    (dict(Nk=1 << 25, H=1, d=128), -1),           # k exceeds 2^31 elements
+])
+def test_decode_validation(lib, kw, status):
+    assert decode(lib, **kw) == status

@@ -451,3 +451,25 @@ def test_oracle_is_independent_of_the_product():
                 src = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
     assert oracle.attention_fwd is attention_fwd
+
+
+@pytest.mark.parametrize("key_len", [None, 5, 0])
+def test_decode_shape_fewer_queries_than_keys(key_len):
+    # Nq != Nk (decode: a few queries against a longer key sequence, no
+    # causal order): the vectorised oracle equals pure-Python loops, and
+    # equals the same rows of the square problem
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((1, 2, 13, 8))
+    k = rng.standard_normal((1, 2, 13, 8))
+    v = rng.standard_normal((1, 2, 13, 8))
+    kl = None if key_len is None else np.array([key_len])
+    rows = [0, 7, 12]
+    O, lse = attention_fwd(q[:, :, rows], k, v, 0.35, key_len=kl)
+    for h in range(2):
+        ob, lb = bruteforce.attention_head(q[0, h, rows].tolist(), k[0, h].tolist(),
+                                           v[0, h].tolist(), 0.35, key_len=key_len)
+        np.testing.assert_allclose(O[0, h], np.array(ob), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[0, h], np.array(lb), rtol=0, atol=1e-12)
+    Of, lf = attention_fwd(q, k, v, 0.35, key_len=kl)
+    np.testing.assert_array_equal(O, Of[:, :, rows])
+    np.testing.assert_array_equal(lse, lf[:, :, rows])

@@ -140,6 +140,17 @@ def make_inputs(w: Workload, seed: int | None = None, N: int | None = None,
                 causal=w.causal)
 
 
+def make_decode_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: int):
+    """Seeded decode inputs: q [B, H, Nq, d] against k, v [B, H, Nk, d]
+    (float32 arrays holding values rounded to ``dtype``), N(0, 1) like the
+    other workloads."""
+    sq, sk, sv = _streams(seed, 3)
+    q = round_to_dtype(sq.standard_normal((B, H, Nq, d), dtype=np.float32), dtype)
+    k = round_to_dtype(sk.standard_normal((B, H, Nk, d), dtype=np.float32), dtype)
+    v = round_to_dtype(sv.standard_normal((B, H, Nk, d), dtype=np.float32), dtype)
+    return dict(q=q, k=k, v=v, scale=1.0 / math.sqrt(d), dtype=dtype)
+
+
 def sample_rows(w: Workload, H: int, N: int, n: int, seed: int | None = None):
     """(h, i) query rows: n drawn uniformly without replacement over all
     heads and positions, plus the forced rows (0, 0) and (H-1, N-1)."""
