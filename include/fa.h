@@ -34,7 +34,7 @@
  *                       or non-positive scale, a workspace that is too small;
  *   FA_ERR_UNSUPPORTED  a valid request this build does not implement
  *                       (d not in {64, 128}, block_size != 128, fp32
- *                       backward, fp32 block-sparse);
+ *                       block-sparse);
  *   FA_ERR_HIP          a kernel launch failed (hipGetLastError).  Faults
  *                       during kernel execution surface at the caller's next
  *                       synchronisation, as for any asynchronous launch.
@@ -103,7 +103,10 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  *   dO      : upstream gradient [B][H][N][d], dtype
  *   dq,dk,dv: outputs [B][H][N][d], dtype (overwritten)
  *   workspace / workspace_bytes: device scratch >= fa_bwd_workspace_size
- * dtype FA_F16 or FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED). */
+ * dtype FA_F16 or FA_BF16 (16-bit matrix-core products on power-of-two
+ * scaled fp16 operands, fp32 accumulation), or FA_F32 (fp32 matrix-core
+ * products, P and dS in fp32; the block-sparse form is FA_ERR_UNSUPPORTED
+ * for fp32). */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dO, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, float scale, int causal,
@@ -134,7 +137,8 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v,
  *   stage FA_BWD_STAGE_D    : the workspace: D_i = sum_c dO_ic O_ic, the
  *                             softmax shift, the per-(b, h) maxima and the
  *                             scaled 16-bit copies of q, k and dO
- *                             (three launches)
+ *                             (three launches; fp32: D and the shift only,
+ *                             one launch)
  *   stage FA_BWD_STAGE_DKDV : dk, dv (reads the workspace written by stage 1)
  *   stage FA_BWD_STAGE_DQ   : dq     (reads the workspace written by stage 1)
  * Running stages 1, 2, 3 in this order on one stream equals fa_bwd.  The

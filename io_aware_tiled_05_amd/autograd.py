@@ -27,7 +27,8 @@ __all__ = ["FlashAttention", "attention", "scaled_dot_product_attention"]
 class FlashAttention(torch.autograd.Function):
     """O = softmax(q k^T * scale + mask) v with the mask given by ``causal``,
     ``key_len`` (keys j >= key_len[b] hidden) or a 128x128 ``block_mask``.
-    q, k, v: contiguous [B, H, N, d] fp16 or bf16 (fp32: forward only)."""
+    q, k, v: contiguous [B, H, N, d] fp32, fp16 or bf16 (block_mask: fp16 or
+    bf16)."""
 
     @staticmethod
     def forward(ctx, q, k, v, scale, causal, key_len, block_mask):

@@ -69,7 +69,7 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
   if (st == FA_OK) st = check_sizes(B, H, N, d);
   if (st != FA_OK) return st;
   if (workspace_bytes < fa_bwd_workspace_size(B, H, N, d)) return FA_ERR_INVALID;
-  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32 && block_mask) return FA_ERR_UNSUPPORTED;
   fa::BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
                 block_mask, workspace, dtype,
                 static_cast<hipStream_t>(stream)};

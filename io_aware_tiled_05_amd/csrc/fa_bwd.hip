@@ -864,6 +864,7 @@ hipError_t dispatch_mask(const BwdArgs& a, int stage) {
 }  // namespace bwd
 
 hipError_t launch_bwd(const BwdArgs& a, int stage) {
+  if (a.dtype == 0) return launch_bwd_f32(a, stage);
   if (a.dtype == 1)
     return a.d == 64 ? bwd::dispatch_mask<_Float16, 64>(a, stage)
                      : bwd::dispatch_mask<_Float16, 128>(a, stage);

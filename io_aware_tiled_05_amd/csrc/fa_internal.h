@@ -125,5 +125,7 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_fwd(const FwdArgs& a);
 // stage 0: all three launches; 1: D only; 2: dK/dV only; 3: dQ only
 hipError_t launch_bwd(const BwdArgs& a, int stage);
+// fp32 inputs (dense, causal, key padding; no block mask); same stages
+hipError_t launch_bwd_f32(const BwdArgs& a, int stage);
 
 }  // namespace fa

@@ -130,7 +130,7 @@ def bwd(lib, blocksparse=False, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dO=None), -1), (dict(dk=None), -1), (dict(ws=None), -1),
     (dict(ws_bytes=WS - 1), -1),                  # workspace too small
-    (dict(d=80), -2), (dict(dtype=F32), -2),
+    (dict(d=80), -2),
     (dict(scale=-1.0), -1), (dict(N=0), -1),
 ])
 def test_bwd_validation(lib, kw, status):
@@ -173,7 +173,7 @@ def stage(lib, st, **kw):
 
 @pytest.mark.parametrize("st,kw,status", [
     (0, {}, -1), (4, {}, -1), (-1, {}, -1),
-    (1, dict(ws=None), -1), (2, dict(d=96), -2), (3, dict(dtype=F32), -2),
+    (1, dict(ws=None), -1), (2, dict(d=96), -2), (3, dict(dtype=F32, bm=P), -2),
     (2, dict(bm=P, causal=1), -1), (2, dict(bm=P, key_len=P), -1), (3, dict(bm=P, bs=64), -2),
     (1, dict(ws_bytes=8), -1),
 ])
