@@ -27,10 +27,12 @@ Modules:
 * :mod:`oracle.bruteforce` — pure-Python loops with ``math.exp``/``math.fsum``
   for tiny shapes.
 
-Every function here is pinned by ``tests/test_oracle.py`` against closed
-forms, invariants, finite differences, a library routine (torch autograd in
-float64 on the CPU) and a hand-derived worked example in ``tests/golden/``.
-Nothing in this package is "parity unpinned".
+Every function here is pinned by ``tests/test_oracle.py`` (and the dropout
+functions by ``tests/test_oracle_dropout.py``) against closed forms,
+invariants, finite differences, a library routine (torch autograd in
+float64 on the CPU), published known-answer vectors of the random number
+generator and a hand-derived worked example in ``tests/golden/``.  Nothing
+in this package is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
@@ -40,4 +42,11 @@ from .attention import (  # noqa: F401
     attention_rows,
     attention_key_grads,
     online_softmax_attention,
+)
+from .dropout import (  # noqa: F401
+    attention_bwd_dropout,
+    attention_fwd_dropout,
+    drop_threshold,
+    keep_mask,
+    philox4x32_10,
 )
