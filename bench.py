@@ -25,6 +25,12 @@ instead times fa_decode (one new query per sequence against a 16384-key
 cache: B=16, H=16, d=64, bf16) and reports the rate at which it streams K
 and V, against MI355X's 8 TB/s HBM: the decode reads each cached key and
 value once and does 4 d flops per key, so it is bound by HBM, not MFMA.
+
+    python bench.py --dropout P [--steps K] [--warmup W]
+
+times the same step with dropout at rate P (fa_fwd_dropout, fa_bwd_dropout;
+the mask drawn from Philox4x32-10 inside the kernels) and reports it with the
+same FLOP count; kernel_ms then holds the forward and the whole backward.
 """
 
 from __future__ import annotations
@@ -216,6 +222,8 @@ def main():
                     help="write profiles/hbm_traffic.json from rocprofv3 --pmc csv files and exit")
     ap.add_argument("--decode", action="store_true",
                     help="time fa_decode on the long-context decode shape instead")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="time the step with dropout at this rate (secondary line, no oracle leg)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, --steps "
                          "times (the known-size kernel that scales the HBM byte counters)")
@@ -264,10 +272,23 @@ def main():
     ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d) // 4, dtype=torch.float32, device=dev)
     scale, causal = x["scale"], w.causal
     stream = torch.cuda.current_stream()
+    drop_p, drop_seed = float(args.dropout), 0x5EED_0001_2345_6789
+    if not 0.0 <= drop_p < 1.0:
+        raise SystemExit("--dropout must be in [0, 1)")
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
+        if drop_p > 0.0:
+            fa.fa_fwd_dropout(q, k, v, drop_p, drop_seed, 0, scale=scale, causal=causal, out=o,
+                              lse=lse)
+            if ev is not None:
+                ev[1].record(stream)
+            fa.fa_bwd_dropout(q, k, v, o, lse, dO, drop_p, drop_seed, 0, scale=scale,
+                              causal=causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+            if ev is not None:
+                ev[2].record(stream)
+            return
         fa.fa_fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
         if ev is not None:
             ev[1].record(stream)
@@ -291,30 +312,37 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(end) / args.steps
-    names = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+    names = ("fwd", "bwd") if drop_p > 0.0 else ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
     kms = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
            for j, nm in enumerate(names)}
 
     P = pairs_of(w)
     fwd_flops, bwd_flops = 4 * d * P, 10 * d * P
     total_tflops = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
-    bwd_ms = kms["bwd_pre"] + kms["bwd_dkdv"] + kms["bwd_dq"]
+    bwd_ms = kms["bwd"] if drop_p > 0.0 else kms["bwd_pre"] + kms["bwd_dkdv"] + kms["bwd_dq"]
     fwd_tflops = fwd_flops / (kms["fwd"] * 1e-3) / 1e12
     bwd_tflops = bwd_flops / (bwd_ms * 1e-3) / 1e12
 
     # dominant kernel and its algorithmic work per launch:
     #   fwd 4 d/pair; dK/dV 8 d/pair (S, dP, dV, dK); dQ 2 d/pair (the dQ
     #   product; its recomputed S and dP repeat work already counted)
-    algo = {"fwd": 4 * d * P, "bwd_dkdv": 8 * d * P, "bwd_dq": 2 * d * P}
-    dom = max(algo, key=lambda nm: kms[nm])
+    #   (with dropout the backward is timed as one: 10 d/pair)
+    algo = {"fwd": 4 * d * P, "bwd_dkdv": 8 * d * P, "bwd_dq": 2 * d * P, "bwd": 10 * d * P}
+    dom = max(kms, key=lambda nm: kms[nm] if nm in algo else 0.0)
     achieved = algo[dom] / (kms[dom] * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(dom)}
+                "traffic": None if drop_p > 0.0 else measured_traffic(dom)}
 
+    metric = "attention fwd+bwd TFLOPS & % MFMA peak, bf16 d=64, N=1K-16K, 1 GPU"
+    config = {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+              "scale": scale, "parallelism": "none (1 GPU)"}
+    if drop_p > 0.0:
+        metric = f"attention fwd+bwd with dropout p={drop_p:g} TFLOPS, bf16 d=64, 1 GPU"
+        config["dropout_p"] = drop_p
     out = {
-        "metric": "attention fwd+bwd TFLOPS & % MFMA peak, bf16 d=64, N=1K-16K, 1 GPU",
+        "metric": metric,
         "value": round(total_tflops, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -326,8 +354,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic N(0,1), seeded",
-        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
-                   "scale": scale, "parallelism": "none (1 GPU)"},
+        "config": config,
         "frac_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),
         "fwd_tflops": round(fwd_tflops, 2),
         "bwd_tflops": round(bwd_tflops, 2),
@@ -336,7 +363,7 @@ def main():
         "kernel_ms": {nm: round(v, 4) for nm, v in kms.items()},
         "wall_s_timed": round(t_wall, 3),
         "roofline": roofline,
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(x, w),
+        "cpu_baseline": None if args.no_cpu_baseline or drop_p > 0.0 else cpu_baseline(x, w),
     }
     print(json.dumps(out), flush=True)
 

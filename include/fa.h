@@ -154,6 +154,31 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v,
                  int block_size, void* workspace, size_t workspace_bytes,
                  int dtype, void* stream);
 
+/* Forward with dropout on the probabilities ([HFL] "Standard Attention
+ * Algorithm" names dropout, with masking and softmax, among the elementwise
+ * passes that dominate standard attention; here it is fused into the
+ * kernel): O = (P * M / (1 - p)) v with M_ij kept iff word j mod 4 of
+ * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011) at counter
+ * (j / 4, i, b*H + h, offset) and key (seed mod 2^32, seed / 2^32) is >=
+ * floor(p 2^32).  lse is that of P (the un-dropped softmax).  The mask
+ * depends only on (seed, offset) and the element's indices, so fa_bwd_dropout
+ * regenerates it instead of storing it.  Other arguments as fa_fwd.
+ *   dropout_p : in [0, 1); 0 gives fa_fwd's result.  Outside: FA_ERR_INVALID
+ * dtype FA_F16 or FA_BF16 (FA_F32 with dropout_p > 0: FA_ERR_UNSUPPORTED). */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const int32_t* key_len, float dropout_p, uint64_t seed, uint32_t offset,
+                   int dtype, void* stream);
+
+/* Backward of fa_fwd_dropout (same dropout_p, seed, offset, and o, lse from
+ * it): dV = (P M')^T dO, dS = P (M' (dO v^T) - D), M' = M / (1 - p).  Other
+ * arguments and the workspace as fa_bwd. */
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv, int B,
+                   int H, int N, int d, float scale, int causal, const int32_t* key_len,
+                   float dropout_p, uint64_t seed, uint32_t offset, void* workspace,
+                   size_t workspace_bytes, int dtype, void* stream);
+
 /* Bytes of device workspace fa_decode needs: one partial result (d + 2
  * floats) per (b, h, query, key chunk), the keys split into chunks of 256 to
  * 1024 rows.  Linear in Nq and Nk.  Returns 0 for invalid sizes. */

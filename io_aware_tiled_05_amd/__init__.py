@@ -16,7 +16,8 @@ from ._lib import (FA_BF16, FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ, 
                    FA_F32, FA_OK, FaError, check, load)
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_fwd_blocksparse", "fa_bwd_blocksparse", "fa_bwd_stage",
-           "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "FaError", "load"]
+           "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd_dropout",
+           "fa_bwd_dropout", "FaError", "load"]
 
 
 def _torch():
@@ -211,3 +212,48 @@ def fa_decode(q, k, v, scale=None, key_len=None, out=None, lse=None, workspace=N
                           _stream(stream))
     check("fa_decode", st)
     return o, lse
+
+
+def _seed(seed, offset):
+    seed, offset = int(seed), int(offset)
+    if not (0 <= seed < 1 << 64 and 0 <= offset < 1 << 32):
+        raise ValueError("seed must fit 64 bits and offset 32 bits (unsigned)")
+    return seed, offset
+
+
+def fa_fwd_dropout(q, k, v, dropout_p, seed, offset=0, scale=None, causal=False, key_len=None,
+                   out=None, lse=None, stream=None):
+    """fa_fwd with dropout on the probabilities; see include/fa.h
+    (fa_fwd_dropout).  Returns (O, lse)."""
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    kl = _key_len(key_len, q)
+    sd, off = _seed(seed, offset)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_qkv(q, o)
+    st = load().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                               _scale(scale, d), int(bool(causal)), _ptr(kl), float(dropout_p),
+                               sd, off, _dtype_code(q), _stream(stream))
+    check("fa_fwd_dropout", st)
+    return o, lse
+
+
+def fa_bwd_dropout(q, k, v, o, lse, dO, dropout_p, seed, offset=0, scale=None, causal=False,
+                   key_len=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward of fa_fwd_dropout (same dropout_p, seed, offset); see
+    include/fa.h (fa_bwd_dropout).  Returns (dq, dk, dv)."""
+    _check_qkv(q, k, v, o, dO)
+    B, H, N, d = q.shape
+    kl = _key_len(key_len, q)
+    sd, off = _seed(seed, offset)
+    dq, dk, dv, ws = _bwd_outputs(q, dq, dk, dv, workspace)
+    _check_qkv(q, dq, dk, dv)
+    st = load().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+                               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d),
+                               int(bool(causal)), _ptr(kl), float(dropout_p), sd, off,
+                               _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(q),
+                               _stream(stream))
+    check("fa_bwd_dropout", st)
+    return dq, dk, dv

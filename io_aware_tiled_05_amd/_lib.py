@@ -27,6 +27,10 @@ SIGNATURES = {
                                 _I, _P, _SZ, _I, _P]),
     "fa_bwd_stage": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P,
                           _P, _I, _P, _SZ, _I, _P]),
+    "fa_fwd_dropout": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _F, C.c_uint64,
+                            C.c_uint32, _I, _P]),
+    "fa_bwd_dropout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _F,
+                            C.c_uint64, C.c_uint32, _P, _SZ, _I, _P]),
     "fa_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _I, _P]),
     "fa_status_string": (C.c_char_p, [_I]),

@@ -37,9 +37,26 @@ int check_dtype(int dtype) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Dropout with probability p in [0, 1): keep iff the element's Philox word
+// is >= floor(p 2^32), scale kept values by 1 / (1 - p).  p = 0 is off.
+int make_dropout(float p, uint64_t seed, uint32_t offset, fa::Dropout* out) {
+  if (!std::isfinite(p) || p < 0.f || p >= 1.f) return FA_ERR_INVALID;
+  fa::Dropout dr;
+  dr.on = p > 0.f;
+  const double t = std::floor((double)p * 4294967296.0);
+  dr.thresh = t >= 4294967295.0 ? 4294967295u : (uint32_t)t;
+  dr.rinv = (float)(1.0 / (1.0 - (double)p));
+  dr.k0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  dr.k1 = (uint32_t)(seed >> 32);
+  dr.offset = offset;
+  *out = dr;
+  return FA_OK;
+}
+
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                int H, int N, int d, float scale, int causal, const int32_t* key_len,
-               const uint8_t* block_mask, int dtype, void* stream) {
+               const uint8_t* block_mask, int dtype, void* stream,
+               const fa::Dropout& drop = fa::Dropout{}) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
@@ -48,8 +65,9 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   if (st == FA_OK) st = check_sizes(B, H, N, d);
   if (st != FA_OK) return st;
   if (block_mask && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (drop.on && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, dtype,
-                static_cast<hipStream_t>(stream)};
+                static_cast<hipStream_t>(stream), drop};
   return hip_status(fa::launch_fwd(a));
 }
 
@@ -57,7 +75,7 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                float scale, int causal, const int32_t* key_len, const uint8_t* block_mask,
                void* workspace, size_t workspace_bytes, int dtype, void* stream,
-               int stage) {
+               int stage, const fa::Dropout& drop = fa::Dropout{}) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
     return FA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
@@ -69,10 +87,10 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
   if (st == FA_OK) st = check_sizes(B, H, N, d);
   if (st != FA_OK) return st;
   if (workspace_bytes < fa_bwd_workspace_size(B, H, N, d)) return FA_ERR_INVALID;
-  if (dtype == FA_F32 && block_mask) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32 && (block_mask || drop.on)) return FA_ERR_UNSUPPORTED;
   fa::BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
                 block_mask, workspace, dtype,
-                static_cast<hipStream_t>(stream)};
+                static_cast<hipStream_t>(stream), drop};
   return hip_status(fa::launch_bwd(a, stage));
 }
 
@@ -147,6 +165,28 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* 
   if (block_size != 128) return block_size < 1 ? FA_ERR_INVALID : FA_ERR_UNSUPPORTED;
   return bwd_common(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, 0, nullptr,
                     block_mask, workspace, workspace_bytes, dtype, stream, 0);
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int N, int d, float scale, int causal, const int32_t* key_len,
+                   float dropout_p, uint64_t seed, uint32_t offset, int dtype, void* stream) {
+  fa::Dropout dr;
+  const int st = make_dropout(dropout_p, seed, offset, &dr);
+  if (st != FA_OK) return st;
+  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, nullptr, dtype,
+                    stream, dr);
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   float scale, int causal, const int32_t* key_len, float dropout_p,
+                   uint64_t seed, uint32_t offset, void* workspace, size_t workspace_bytes,
+                   int dtype, void* stream) {
+  fa::Dropout dr;
+  const int st = make_dropout(dropout_p, seed, offset, &dr);
+  if (st != FA_OK) return st;
+  return bwd_common(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
+                    nullptr, workspace, workspace_bytes, dtype, stream, 0, dr);
 }
 
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d) {

@@ -278,6 +278,7 @@ struct BwdParams {
   uint16_t* dv;
   int H, N, BH, ntiles;
   int period;  // snake period of map_workgroup (0: plain order)
+  Dropout drop;  // used by the DROP kernels only
   float c;      // scale * log2(e)
   float scale;
   const int32_t* key_len;
@@ -338,7 +339,8 @@ __device__ __forceinline__ int list_blocks(const uint8_t* m, int stride, int w0,
 // ---------------------------------------------------------------------------
 // T is the input/output type; the products run on the scaled fp16 operands
 // described at the top of this file.
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+// DROP: dropout on P (dV uses P M / (1 - p), dS = P (dP M / (1 - p) - D))
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32, TILE = kBQ * D, NW = 4;
   typedef _Float16 TI;
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           s[qb][4 * i + j] = a4[j];
-          dp[qb][4 * i + j] = b4[j];
+          dp[qb][4 * i + j] = DROP ? 0.f : b4[j];  // with dropout -D enters after the mask
         }
       }
 #pragma unroll
@@ -445,7 +447,32 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
     // The visibility test is hoisted out of the element loop and done with
     // selects: query q0 + 32qb + 4h + o, o = 8(e/4) + e%4, sees this lane's
     // key iff lo <= o < hi.
-    if (need_mask) {
+    if constexpr (DROP) {
+      // each element has its own word: element e is query q0 + 32qb + 8(e/4) +
+      // 4h + e%4 of this lane's key, word key % 4 of its counter
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qbase = q0 + qb * 32 + 4 * h;
+        const int hi = key < L ? N - qbase : -64;
+        const int lo = CAUSAL ? key - qbase : -64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 nd4 = *reinterpret_cast<const f32x4*>(td + qb * 32 + 8 * i + 4 * h);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int o = 8 * i + j, e = 4 * i + j;
+            const float pv = ((o >= lo) & (o < hi)) ? fast_exp2(s[qb][e]) : 0.f;
+            uint32_t w[4];
+            philox4x32_10((uint32_t)key >> 2, (uint32_t)(qbase + o), (uint32_t)bh,
+                          p.drop.offset, p.drop.k0, p.drop.k1, w);
+            const uint32_t wk = (key & 2) ? ((key & 1) ? w[3] : w[2]) : ((key & 1) ? w[1] : w[0]);
+            const float mk = wk >= p.drop.thresh ? p.drop.rinv : 0.f;
+            dp[qb][e] = pv * fmaf(mk, dp[qb][e], nd4[j]);
+            s[qb][e] = pv * mk;
+          }
+        }
+      }
+    } else if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int qbase = q0 + qb * 32 + 4 * h;
@@ -559,7 +586,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
 // three bf16 parts, so the accumulators end as the exponent of P and as
 // dP - D: P is one exponential and dS one multiply.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+// DROP: dS = P (dP M / (1 - p) - D); the -D k-step is left out
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32, TILE = kBC * D, NW = 4;
   typedef _Float16 TI;
@@ -584,6 +612,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
   const int L = valid_keys(p.key_len, b, N);
   const int q0 = qt * kBR, qw = q0 + wave * 32, query = qw + l32;
   const Scales sc = bwd_scales(p.maxes, p.BH, bh, p.c);
+  // D of this lane's query (dropout: subtracted after the mask)
+  const float dq_D = DROP && query < N ? p.Dbuf[(size_t)bh * N + query] : 0.f;
 
   // this wave's queries (c Q 2^-eq, fp16) and output gradients as B
   // operands (lane = query, k = d values)
@@ -647,7 +677,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = dp[kb][e] = 0.f;
       s[kb] = Elt<__bf16>::mfma32(one_b, s_aug_b, s[kb]);
-      dp[kb] = Elt<__bf16>::mfma32(one_b, d_aug_b, dp[kb]);
+      if constexpr (!DROP) dp[kb] = Elt<__bf16>::mfma32(one_b, d_aug_b, dp[kb]);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -667,7 +697,28 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
     }
     // key kt0 + 32kb + 4h + o, o = 8(e/4) + e%4, is visible to this lane's
     // query iff o <= thr (the test hoisted out of the element loop, selects)
-    if (need_mask) {
+    if constexpr (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kbase = kt0 + kb * 32 + 4 * h;
+        int thr = L - 1 - kbase;
+        if (CAUSAL) thr = min(thr, query - kbase);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // elements 4i .. 4i+3: keys kbase + 8i + 0..3, one counter
+          uint32_t w[4];
+          philox4x32_10((uint32_t)(kbase + 8 * i) >> 2, (uint32_t)query, (uint32_t)bh,
+                        p.drop.offset, p.drop.k0, p.drop.k1, w);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = 4 * i + j;
+            const float pv = 8 * i + j <= thr ? fast_exp2(s[kb][e]) : 0.f;
+            const float mk = w[j] >= p.drop.thresh ? p.drop.rinv : 0.f;
+            dp[kb][e] = pv * fmaf(mk, dp[kb][e], -dq_D);
+          }
+        }
+      }
+    } else if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int kbase = kt0 + kb * 32 + 4 * h;
@@ -759,12 +810,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
   template __global__ void bwd_pre_kernel<T, D, true>(                            \
       const uint16_t*, const uint16_t*, const float*, const uint16_t*, const uint16_t*, \
       const uint16_t*, float*, float*, uint32_t*, int, int);                        \
-  template __global__ void bwd_dkdv_kernel<T, D, true, false>(BwdParams);          \
-  template __global__ void bwd_dkdv_kernel<T, D, false, false>(BwdParams);         \
-  template __global__ void bwd_dkdv_kernel<T, D, false, true>(BwdParams);          \
-  template __global__ void bwd_dq_kernel<T, D, true, false>(BwdParams);            \
-  template __global__ void bwd_dq_kernel<T, D, false, false>(BwdParams);           \
-  template __global__ void bwd_dq_kernel<T, D, false, true>(BwdParams);          \
+  template __global__ void bwd_dkdv_kernel<T, D, true, false, false>(BwdParams);   \
+  template __global__ void bwd_dkdv_kernel<T, D, false, false, false>(BwdParams);  \
+  template __global__ void bwd_dkdv_kernel<T, D, false, true, false>(BwdParams);   \
+  template __global__ void bwd_dkdv_kernel<T, D, true, false, true>(BwdParams);    \
+  template __global__ void bwd_dkdv_kernel<T, D, false, false, true>(BwdParams);   \
+  template __global__ void bwd_dq_kernel<T, D, true, false, false>(BwdParams);     \
+  template __global__ void bwd_dq_kernel<T, D, false, false, false>(BwdParams);    \
+  template __global__ void bwd_dq_kernel<T, D, true, false, true>(BwdParams);      \
+  template __global__ void bwd_dq_kernel<T, D, false, false, true>(BwdParams);     \
+  template __global__ void bwd_dq_kernel<T, D, false, true, false>(BwdParams);          \
   template __global__ void bwd_convert_kernel<T, D>(                               \
       const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*,   \
       const uint32_t*, float,                                                        \
@@ -775,7 +830,7 @@ FA_BWD_INSTANTIATE(_Float16, 64)
 FA_BWD_INSTANTIATE(_Float16, 128)
 #undef FA_BWD_INSTANTIATE
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t run_bwd(const BwdArgs& a, int stage) {
   hipError_t e = hipSuccess;
   const int64_t rows = (int64_t)a.B * a.H * a.N;
@@ -838,17 +893,18 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   p.block_mask = a.block_mask;
   p.nblk = (a.N + 127) / 128;
   p.period = (FA_BWD_SNAKE && CAUSAL) ? snake_period(p.BH) : 0;
+  p.drop = a.drop;
 
   if (stage == 0 || stage == 2) {
     p.ntiles = (a.N + kBKV - 1) / kBKV;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, SPARSE>), dim3(p.ntiles * p.BH),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(p.ntiles * p.BH),
                        dim3(256), 0, a.stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stage == 0 || stage == 3) {
     p.ntiles = (a.N + kBR - 1) / kBR;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, SPARSE>), dim3(p.ntiles * p.BH),
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(p.ntiles * p.BH),
                        dim3(256), 0, a.stream, p);
     e = hipGetLastError();
   }
@@ -857,8 +913,12 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
 
 template <typename T, int D>
 hipError_t dispatch_mask(const BwdArgs& a, int stage) {
-  if (a.block_mask) return run_bwd<T, D, false, true>(a, stage);
-  return a.causal ? run_bwd<T, D, true, false>(a, stage) : run_bwd<T, D, false, false>(a, stage);
+  if (a.block_mask) return run_bwd<T, D, false, true, false>(a, stage);
+  if (a.drop.on)
+    return a.causal ? run_bwd<T, D, true, false, true>(a, stage)
+                    : run_bwd<T, D, false, false, true>(a, stage);
+  return a.causal ? run_bwd<T, D, true, false, false>(a, stage)
+                  : run_bwd<T, D, false, false, false>(a, stage);
 }
 
 }  // namespace bwd

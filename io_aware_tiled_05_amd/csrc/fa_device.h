@@ -233,6 +233,34 @@ struct TileCopy {
   }
 };
 
+// Philox4x32-10, the counter-based generator of J. K. Salmon, M. A. Moraes,
+// R. O. Dror and D. E. Shaw ("Parallel random numbers: as easy as 1, 2,
+// 3", SC 2011): ten rounds, each multiplying counter words 0 and 2 by the
+// round multipliers into 64-bit products and forming (hi1 ^ c1 ^ k0, lo1,
+// hi0 ^ c3 ^ k1, lo0); the key is bumped by the Weyl increments between
+// rounds.  Four 32-bit outputs per counter.
+__host__ __device__ inline void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                         uint32_t c3, uint32_t k0, uint32_t k1,
+                                         uint32_t (&w)[4]) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  w[0] = c0;
+  w[1] = c1;
+  w[2] = c2;
+  w[3] = c3;
+}
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 __device__ __forceinline__ float pos_inf() { return __builtin_huge_valf(); }
 

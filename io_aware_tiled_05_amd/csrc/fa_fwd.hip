@@ -48,6 +48,7 @@ struct FwdParams {
   const int32_t* key_len;
   const uint8_t* block_mask;
   int nblk;
+  Dropout drop;  // used by the DROP kernels only
 };
 
 // Compile-time tuning knobs (defaults are the measured best).
@@ -79,10 +80,15 @@ struct FwdShape {
 };
 
 // NW waves per workgroup; a workgroup covers NW * QW queries.
-template <typename T, int D, int NW, bool CAUSAL, bool SPARSE>
+// DROP: dropout on P before the product with V (P kept with probability
+// 1 - p and scaled by 1 / (1 - p); the row sum l and lse use P itself).
+template <typename T, int D, int NW, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(FwdParams p) {
   typedef FwdShape<D> Sh;
-  constexpr int QW = Sh::QW, NQB = Sh::NQB, KS = Sh::KS, DB = Sh::DB, TILE = Sh::TILE;
+  // with dropout a wave takes 32 queries (the generator's registers do not
+  // fit next to two query blocks)
+  constexpr int QW = DROP ? 32 : Sh::QW, NQB = QW / 32, KS = Sh::KS, DB = Sh::DB;
+  constexpr int TILE = Sh::TILE;
   constexpr int BR = NW * QW;
   typedef typename Elt<T>::vec8 vec8;
   // two K and two V tile buffers, separate arrays so that the compiler can
@@ -200,14 +206,30 @@ __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(Fwd
       auto exp_pack = [&](int qb, float msc) {
         float r[4] = {0.f, 0.f, 0.f, 0.f};  // four independent sum chains
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};  // dropout words of the current 4 keys
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float x0 = fast_exp2(fmaf(s[kb][qb][2 * e], c, -msc));
-            const float x1 = fast_exp2(fmaf(s[kb][qb][2 * e + 1], c, -msc));
-            pk[kb][qb][e] = Elt<T>::pack2(x0, x1);
-            r[e & 3] = Elt<T>::sum2(pk[kb][qb][e], r[e & 3]);
+            float x0 = fast_exp2(fmaf(s[kb][qb][2 * e], c, -msc));
+            float x1 = fast_exp2(fmaf(s[kb][qb][2 * e + 1], c, -msc));
+            if constexpr (DROP) {
+              // elements 4i .. 4i+3 are keys kt0 + 32 kb + 8i + 4h + 0..3
+              if ((e & 1) == 0)
+                philox4x32_10((uint32_t)(kt0 + kb * 32 + 8 * (e >> 1) + 4 * h) >> 2,
+                              (uint32_t)(qw + qb * 32 + l32), (uint32_t)bh, p.drop.offset,
+                              p.drop.k0, p.drop.k1, w);
+              r[(2 * e) & 3] += x0;
+              r[(2 * e + 1) & 3] += x1;
+              const int j = 2 * (e & 1);
+              x0 = w[j] >= p.drop.thresh ? x0 * p.drop.rinv : 0.f;
+              x1 = w[j + 1] >= p.drop.thresh ? x1 * p.drop.rinv : 0.f;
+              pk[kb][qb][e] = Elt<T>::pack2(x0, x1);
+            } else {
+              pk[kb][qb][e] = Elt<T>::pack2(x0, x1);
+              r[e & 3] = Elt<T>::sum2(pk[kb][qb][e], r[e & 3]);
+            }
           }
+        }
         rs[qb] = (r[0] + r[1]) + (r[2] + r[3]);
       };
       bool over = false;
@@ -482,9 +504,12 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParamsF32 p) {
 // (Without them the host pass of this compiler leaves some kernel-template
 // launch stubs undefined.)
 #define FA_FWD_INSTANTIATE(T, D)                                                              \
-  template __global__ void fwd_kernel<T, D, 128 / FwdShape<D>::QW, false, true>(FwdParams);  \
-  template __global__ void fwd_kernel<T, D, 4, true, false>(FwdParams);                      \
-  template __global__ void fwd_kernel<T, D, 4, false, false>(FwdParams);
+  template __global__ void fwd_kernel<T, D, 128 / FwdShape<D>::QW, false, true, false>(      \
+      FwdParams);                                                                            \
+  template __global__ void fwd_kernel<T, D, 4, true, false, false>(FwdParams);               \
+  template __global__ void fwd_kernel<T, D, 4, false, false, false>(FwdParams);              \
+  template __global__ void fwd_kernel<T, D, 4, true, false, true>(FwdParams);                \
+  template __global__ void fwd_kernel<T, D, 4, false, false, true>(FwdParams);
 
 FA_FWD_INSTANTIATE(__bf16, 64)
 FA_FWD_INSTANTIATE(__bf16, 128)
@@ -496,10 +521,10 @@ template __global__ void fwd_f32_kernel<64, false>(FwdParamsF32);
 template __global__ void fwd_f32_kernel<128, true>(FwdParamsF32);
 template __global__ void fwd_f32_kernel<128, false>(FwdParamsF32);
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t run_fwd(const FwdArgs& a) {
   // block-sparse workgroups cover exactly one 128-query mask row
-  constexpr int QW = FwdShape<D>::QW;
+  constexpr int QW = DROP ? 32 : FwdShape<D>::QW;
   constexpr int NW = SPARSE ? 128 / QW : 4;
   constexpr int BR = NW * QW;
   FwdParams p;
@@ -517,8 +542,9 @@ hipError_t run_fwd(const FwdArgs& a) {
   p.key_len = a.key_len;
   p.block_mask = a.block_mask;
   p.nblk = (a.N + 127) / 128;
+  p.drop = a.drop;
   const int wgs_per_head = CAUSAL && !SPARSE ? (p.nqt + 1) / 2 : p.nqt;
-  hipLaunchKernelGGL((fwd_kernel<T, D, NW, CAUSAL, SPARSE>), dim3(wgs_per_head * p.BH),
+  hipLaunchKernelGGL((fwd_kernel<T, D, NW, CAUSAL, SPARSE, DROP>), dim3(wgs_per_head * p.BH),
                      dim3(64 * NW),
                      0, a.stream, p);
   return hipGetLastError();
@@ -545,8 +571,10 @@ hipError_t run_fwd_f32(const FwdArgs& a) {
 
 template <typename T, int D>
 hipError_t dispatch_mask(const FwdArgs& a) {
-  if (a.block_mask) return run_fwd<T, D, false, true>(a);
-  return a.causal ? run_fwd<T, D, true, false>(a) : run_fwd<T, D, false, false>(a);
+  if (a.block_mask) return run_fwd<T, D, false, true, false>(a);
+  if (a.drop.on)
+    return a.causal ? run_fwd<T, D, true, false, true>(a) : run_fwd<T, D, false, false, true>(a);
+  return a.causal ? run_fwd<T, D, true, false, false>(a) : run_fwd<T, D, false, false, false>(a);
 }
 
 }  // namespace fwd

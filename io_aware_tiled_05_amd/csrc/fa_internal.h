@@ -8,6 +8,16 @@
 
 namespace fa {
 
+// Dropout on the probabilities (off unless `on`): element (b, h, i, j) is
+// kept iff word j mod 4 of Philox4x32-10(counter = (j div 4, i, b H + h,
+// offset), key = (k0, k1)) is >= thresh; kept values are multiplied by rinv.
+struct Dropout {
+  int on = 0;
+  uint32_t thresh = 0;
+  float rinv = 1.f;
+  uint32_t k0 = 0, k1 = 0, offset = 0;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -21,6 +31,7 @@ struct FwdArgs {
   const uint8_t* block_mask; // nullable; [nb][nb], block 128
   int dtype;                 // fa_dtype
   hipStream_t stream;
+  Dropout drop = {};
 };
 
 struct BwdArgs {
@@ -41,6 +52,7 @@ struct BwdArgs {
   void* workspace;           // bwd_workspace_layout(B, H, N, d).total bytes
   int dtype;
   hipStream_t stream;
+  Dropout drop = {};
 };
 
 // Backward workspace, regions 256-byte aligned, in this order:

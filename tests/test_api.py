@@ -30,8 +30,9 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_decode",
-        "fa_decode_workspace_size", "fa_fwd", "fa_fwd_blocksparse", "fa_status_string"])
+        "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_dropout", "fa_bwd_stage", "fa_bwd_workspace_size",
+        "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_blocksparse",
+        "fa_fwd_dropout", "fa_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -208,3 +209,26 @@ def decode(lib, **kw):
 ])
 def test_decode_validation(lib, kw, status):
     assert decode(lib, **kw) == status
+
+
+def fwd_drop(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, scale=0.125, causal=0,
+             key_len=None, p=0.1, seed=1, offset=0, dtype=BF16)
+    a.update(kw)
+    return lib.fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                              a["d"], a["scale"], a["causal"], a["key_len"], a["p"], a["seed"],
+                              a["offset"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=-0.1), -1), (dict(p=1.0), -1), (dict(p=float("nan")), -1), (dict(q=None), -1),
+    (dict(dtype=F32), -2), (dict(d=96), -2),
+])
+def test_dropout_validation(lib, kw, status):
+    assert fwd_drop(lib, **kw) == status
+    b = dict(p=0.1, dtype=BF16, d=64)
+    b.update({k: v for k, v in kw.items() if k in ("p", "dtype", "d")})
+    st = lib.fa_bwd_dropout(P, P, P, P, P, P, P, P, P, 2, 2, 256, b["d"], 0.125, 0, None, b["p"],
+                            1, 0, P, WS, b["dtype"], None)
+    if "q" not in kw:
+        assert st == status

@@ -114,7 +114,9 @@ def test_argument_errors_before_gpu_work():
     from io_aware_tiled_05_amd.autograd import attention, scaled_dot_product_attention
     t = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError, match="dropout"):
-        scaled_dot_product_attention(t, t, t, dropout_p=0.1)
+        scaled_dot_product_attention(t, t, t, dropout_p=1.0)
+    with pytest.raises(ValueError, match="dropout"):
+        attention(t, t, t, dropout_p=0.1, block_mask=torch.ones(1, 1, dtype=torch.uint8))
     with pytest.raises(ValueError, match="attn_mask"):
         scaled_dot_product_attention(t, t, t, attn_mask=torch.zeros(4, 4))
     with pytest.raises(ValueError, match="layout"):
