@@ -448,8 +448,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
     // selects: query q0 + 32qb + 4h + o, o = 8(e/4) + e%4, sees this lane's
     // key iff lo <= o < hi.
     if constexpr (DROP) {
-      // each element has its own word: element e is query q0 + 32qb + 8(e/4) +
-      // 4h + e%4 of this lane's key, word key % 4 of its counter
+      // Element e is query q0 + 32qb + 8(e/4) + 4h + e%4 of this lane's key:
+      // word key % 4 of the counter (key / 4, query).  The four lanes of a
+      // quad hold keys 4m .. 4m + 3 and the same four queries of each
+      // (qb, e/4) block, so lane t draws the counter of the block's query t
+      // (its four words are the four keys' draws), turns them into four
+      // keep bits, and the quad exchanges the bits: bit 4j + t of the OR is
+      // key 4m + t at query j.  One generator call per four elements.
+      const int t = lane & 3;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int qbase = q0 + qb * 32 + 4 * h;
@@ -458,15 +464,18 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const f32x4 nd4 = *reinterpret_cast<const f32x4*>(td + qb * 32 + 8 * i + 4 * h);
+          uint32_t w[4];
+          philox4x32_10((uint32_t)key >> 2, (uint32_t)(qbase + 8 * i + t), (uint32_t)bh,
+                        p.drop.offset, p.drop.k0, p.drop.k1, w);
+          const uint32_t th = p.drop.thresh;
+          const uint32_t nib = (w[0] >= th ? 1u : 0u) | (w[1] >= th ? 2u : 0u) |
+                               (w[2] >= th ? 4u : 0u) | (w[3] >= th ? 8u : 0u);
+          const uint32_t bits = quad_or(nib << (4 * t)) >> t;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int o = 8 * i + j, e = 4 * i + j;
             const float pv = ((o >= lo) & (o < hi)) ? fast_exp2(s[qb][e]) : 0.f;
-            uint32_t w[4];
-            philox4x32_10((uint32_t)key >> 2, (uint32_t)(qbase + o), (uint32_t)bh,
-                          p.drop.offset, p.drop.k0, p.drop.k1, w);
-            const uint32_t wk = (key & 2) ? ((key & 1) ? w[3] : w[2]) : ((key & 1) ? w[1] : w[0]);
-            const float mk = wk >= p.drop.thresh ? p.drop.rinv : 0.f;
+            const float mk = (bits >> (4 * j)) & 1u ? p.drop.rinv : 0.f;
             dp[qb][e] = pv * fmaf(mk, dp[qb][e], nd4[j]);
             s[qb][e] = pv * mk;
           }

@@ -233,6 +233,15 @@ struct TileCopy {
   }
 };
 
+// OR of v over the four lanes of a quad (lanes 4q .. 4q + 3), in every lane
+// of it: two DPP quad permutations, swapping neighbours and then pairs.
+// Every lane of the wave must be active.
+__device__ inline uint32_t quad_or(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  return v;
+}
+
 // Philox4x32-10, the counter-based generator of J. K. Salmon, M. A. Moraes,
 // R. O. Dror and D. E. Shaw ("Parallel random numbers: as easy as 1, 2,
 // 3", SC 2011): ten rounds, each multiplying counter words 0 and 2 by the
