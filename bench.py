@@ -336,10 +336,12 @@ def main():
                 "traffic": None if drop_p > 0.0 else measured_traffic(dom)}
 
     metric = "attention fwd+bwd TFLOPS & % MFMA peak, bf16 d=64, N=1K-16K, 1 GPU"
+    if d != 64:
+        metric = metric.replace("d=64", f"d={d}")
     config = {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
               "scale": scale, "parallelism": "none (1 GPU)"}
     if drop_p > 0.0:
-        metric = f"attention fwd+bwd with dropout p={drop_p:g} TFLOPS, bf16 d=64, 1 GPU"
+        metric = f"attention fwd+bwd with dropout p={drop_p:g} TFLOPS, bf16 d={d}, 1 GPU"
         config["dropout_p"] = drop_p
     out = {
         "metric": metric,

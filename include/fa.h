@@ -25,7 +25,7 @@
  *   float32 [B][H][N] array (natural logarithm).  key_len is int32 [B] in
  *   device memory.  block_mask is uint8 [nb][nb] in device memory,
  *   nb = ceil(N / block_size), shared by every (b, h).
- * Sizes.  B >= 1, H >= 1, N >= 1, d in {64, 128}; B*H <= 65535*65535 and
+ * Sizes.  B >= 1, H >= 1, N >= 1, d in {32, 64, 96, 128}; B*H <= 65535*65535 and
  *   B*H*N*d < 2^31 elements per tensor.
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls
  *   only enqueue work on it and return without synchronising.
@@ -33,7 +33,7 @@
  *   FA_ERR_INVALID      a null pointer, a size out of range, a non-finite
  *                       or non-positive scale, a workspace that is too small;
  *   FA_ERR_UNSUPPORTED  a valid request this build does not implement
- *                       (d not in {64, 128}, block_size != 128, fp32
+ *                       (d not in {32, 64, 96, 128}, block_size != 128, fp32
  *                       block-sparse);
  *   FA_ERR_HIP          a kernel launch failed (hipGetLastError).  Faults
  *                       during kernel execution surface at the caller's next
@@ -196,7 +196,7 @@ size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d);
  *   lse     : [B][H][Nq] fp32 (natural log; -inf and O = 0 for a query
  *             without visible keys)
  *   workspace / workspace_bytes: device scratch >= fa_decode_workspace_size
- * dtype FA_F32, FA_F16 or FA_BF16; d 64 or 128.  Products and the softmax
+ * dtype FA_F32, FA_F16 or FA_BF16; d 32, 64, 96 or 128.  Products and the softmax
  * run in fp32.  Errors as for fa_fwd (a small workspace is
  * FA_ERR_INVALID). */
 int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

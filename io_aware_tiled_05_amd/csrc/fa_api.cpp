@@ -21,7 +21,7 @@ int check_sizes(int B, int H, int N, int d) {
   if (bh * N * d > kMaxElems) return FA_ERR_INVALID;
   // grid size: one workgroup per 128 rows per head
   if (bh * ((int64_t(N) + 127) / 128) > kMaxElems) return FA_ERR_INVALID;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

@@ -152,16 +152,24 @@ __device__ __forceinline__ uint32_t absmax8(u32x4 a) {
 // ---------------------------------------------------------------------------
 constexpr int kPreIter = 16;  // row groups per workgroup in the D pass
 
+// threads per row in the D pass: one per 8 elements (16 bytes), rounded up
+// to a power of two for the shuffle reduction (d = 96: 16, the last 4 idle)
+template <int D>
+constexpr int pre_tpr() {
+  return D / 8 <= 4 ? 4 : D / 8 <= 8 ? 8 : 16;
+}
+
 template <typename T, int D, bool STATS>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const uint16_t* dO,
                                                       const float* lse, const uint16_t* q,
                                                       const uint16_t* k, const uint16_t* v,
                                                       float* Dbuf, float* shift,
                                                       uint32_t* maxes, int N, int BH) {
-  constexpr int TPR = D / 8;  // threads per row, 8 elements (16 B) each
-  constexpr int RPB = 256 / TPR;  // rows per pass of the workgroup
+  constexpr int TPR = pre_tpr<D>();  // threads per row, 8 elements (16 B) each
+  constexpr int RPB = 256 / TPR;      // rows per pass of the workgroup
   const int bh = blockIdx.x;
   const int c = (int)(threadIdx.x % TPR) * 8;
+  const bool col_ok = c < D;
   uint32_t mx[4] = {0u, 0u, 0u, 0u};
   const int r_begin = blockIdx.y * RPB * kPreIter;
 #pragma unroll 4
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
     const bool ok = r < N;
     const int64_t row = (int64_t)bh * N + r;
     float s = 0.f;
-    if (ok) {
+    if (ok && col_ok) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + c);
       const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + c);
 #pragma unroll
@@ -341,7 +349,7 @@ __device__ __forceinline__ int list_blocks(const uint8_t* m, int stride, int w0,
 // described at the top of this file.
 // DROP: dropout on P (dV uses P M / (1 - p), dS = P (dP M / (1 - p) - D))
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32, TILE = kBQ * D, NW = 4;
   typedef _Float16 TI;
   typedef typename Elt<TI>::vec8 vec8;
@@ -597,7 +605,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
 // ---------------------------------------------------------------------------
 // DROP: dS = P (dP M / (1 - p) - D); the -D k-step is left out
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32, TILE = kBC * D, NW = 4;
   typedef _Float16 TI;
   typedef typename Elt<TI>::vec8 hvec8;
@@ -833,9 +841,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
       const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*,   \
       const uint32_t*, float,                                                        \
       uint16_t*, uint16_t*, uint16_t*, float*, float*, int64_t, int, int);
+FA_BWD_INSTANTIATE(__bf16, 32)
 FA_BWD_INSTANTIATE(__bf16, 64)
+FA_BWD_INSTANTIATE(__bf16, 96)
 FA_BWD_INSTANTIATE(__bf16, 128)
+FA_BWD_INSTANTIATE(_Float16, 32)
 FA_BWD_INSTANTIATE(_Float16, 64)
+FA_BWD_INSTANTIATE(_Float16, 96)
 FA_BWD_INSTANTIATE(_Float16, 128)
 #undef FA_BWD_INSTANTIATE
 
@@ -863,7 +875,7 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
                        maxes, 4 * BH);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    constexpr int pre_rows = 256 / (D / 8) * kPreIter;  // rows per workgroup
+    constexpr int pre_rows = 256 / pre_tpr<D>() * kPreIter;  // rows per workgroup
     hipLaunchKernelGGL((bwd_pre_kernel<T, D, true>), dim3(BH, (a.N + pre_rows - 1) / pre_rows),
                        dim3(256), 0, a.stream, static_cast<const uint16_t*>(a.o), dO, a.lse, q,
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), Dbuf,
@@ -932,13 +944,22 @@ hipError_t dispatch_mask(const BwdArgs& a, int stage) {
 
 }  // namespace bwd
 
+namespace bwd {
+template <typename T>
+hipError_t dispatch_dim(const BwdArgs& a, int stage) {
+  switch (a.d) {
+    case 32: return dispatch_mask<T, 32>(a, stage);
+    case 64: return dispatch_mask<T, 64>(a, stage);
+    case 96: return dispatch_mask<T, 96>(a, stage);
+    default: return dispatch_mask<T, 128>(a, stage);
+  }
+}
+}  // namespace bwd
+
 hipError_t launch_bwd(const BwdArgs& a, int stage) {
   if (a.dtype == 0) return launch_bwd_f32(a, stage);
-  if (a.dtype == 1)
-    return a.d == 64 ? bwd::dispatch_mask<_Float16, 64>(a, stage)
-                     : bwd::dispatch_mask<_Float16, 128>(a, stage);
-  return a.d == 64 ? bwd::dispatch_mask<__bf16, 64>(a, stage)
-                   : bwd::dispatch_mask<__bf16, 128>(a, stage);
+  if (a.dtype == 1) return bwd::dispatch_dim<_Float16>(a, stage);
+  return bwd::dispatch_dim<__bf16>(a, stage);
 }
 
 }  // namespace fa

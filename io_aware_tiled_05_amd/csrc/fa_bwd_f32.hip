@@ -254,7 +254,9 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
   template __global__ void dkdv_kernel<D, false>(Params);                              \
   template __global__ void dq_kernel<D, true>(Params);                                 \
   template __global__ void dq_kernel<D, false>(Params);
+FA_BWD32_INSTANTIATE(32)
 FA_BWD32_INSTANTIATE(64)
+FA_BWD32_INSTANTIATE(96)
 FA_BWD32_INSTANTIATE(128)
 #undef FA_BWD32_INSTANTIATE
 
@@ -307,8 +309,12 @@ hipError_t run(const BwdArgs& a, int stage) {
 
 hipError_t launch_bwd_f32(const BwdArgs& a, int stage) {
   using namespace bwd32;
-  if (a.d == 64) return a.causal ? run<64, true>(a, stage) : run<64, false>(a, stage);
-  return a.causal ? run<128, true>(a, stage) : run<128, false>(a, stage);
+  switch (a.d) {
+    case 32: return a.causal ? run<32, true>(a, stage) : run<32, false>(a, stage);
+    case 64: return a.causal ? run<64, true>(a, stage) : run<64, false>(a, stage);
+    case 96: return a.causal ? run<96, true>(a, stage) : run<96, false>(a, stage);
+    default: return a.causal ? run<128, true>(a, stage) : run<128, false>(a, stage);
+  }
 }
 
 }  // namespace fa

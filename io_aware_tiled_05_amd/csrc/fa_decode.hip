@@ -96,7 +96,9 @@ __device__ __forceinline__ float rel_exp2(float a, float b) {
 // grid: x = chunk + nchunks * bh, y = query group; 256 threads
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
-  constexpr int LPK = D / 8;      // lanes per key row
+  // lanes per key row: one per 8 elements, rounded up to a power of two for
+  // the shuffle reductions (d = 96: 16 lanes, the last 4 hold no elements)
+  constexpr int LPK = D / 8 <= 4 ? 4 : D / 8 <= 8 ? 8 : 16;
   constexpr int KPW = 64 / LPK;   // keys per wave and step
   constexpr int EB = Ld<T>::ES;   // bytes per element
   __shared__ float sm[4][kQG], sl[4][kQG];
@@ -114,6 +116,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
     L = kl < 0 ? 0 : (kl > p.Nk ? p.Nk : kl);
   }
   const int slot = lane / LPK, dsl = (lane % LPK) * 8;
+  const bool dok = dsl < D;  // this lane holds a d-slice
   // this wave's keys: a quarter of the chunk
   const int wlen = p.chunk / 4;
   const int kb = chunk * p.chunk + wave * wlen;
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   float qv[kQG][8];
 #pragma unroll
   for (int i = 0; i < kQG; ++i) {
-    if (i < nq) {
+    if (i < nq && dok) {
       const size_t off = (((size_t)bh * p.Nq + q0 + i) * D + dsl) * (EB / 2);
       load8<T>(p.q + off, qv[i]);
 #pragma unroll
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
     for (int u = 0; u < U; ++u) {
       const int key = k0 + u * KPW + slot;
       ok[u] = key < ke;
-      if (ok[u]) {
+      if (ok[u] && dok) {
         const size_t off = (kvbase + (size_t)key * D + dsl) * (EB / 2);
         Ld<T>::load(p.k + off, kr[u]);
         Ld<T>::load(p.v + off, vr[u]);
@@ -208,8 +211,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   if (slot == 0) {
 #pragma unroll
     for (int i = 0; i < kQG; ++i) {
+      if (dok)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sO[wave][i][dsl + e] = o[i][e];
+        for (int e = 0; e < 8; ++e) sO[wave][i][dsl + e] = o[i][e];
       if (lane == 0) {
         sm[wave][i] = m[i];
         sl[wave][i] = l[i];
@@ -270,12 +274,13 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* part, uint
 #define FA_DEC_INSTANTIATE(T, D)                                                  \
   template __global__ void decode_partial_kernel<T, D>(DecodeParams);            \
   template __global__ void decode_merge_kernel<T, D>(const float*, uint16_t*, float*, int);
-FA_DEC_INSTANTIATE(__bf16, 64)
-FA_DEC_INSTANTIATE(__bf16, 128)
-FA_DEC_INSTANTIATE(_Float16, 64)
-FA_DEC_INSTANTIATE(_Float16, 128)
-FA_DEC_INSTANTIATE(float, 64)
-FA_DEC_INSTANTIATE(float, 128)
+#define FA_DEC_INSTANTIATE_D(D) \
+  FA_DEC_INSTANTIATE(__bf16, D) FA_DEC_INSTANTIATE(_Float16, D) FA_DEC_INSTANTIATE(float, D)
+FA_DEC_INSTANTIATE_D(32)
+FA_DEC_INSTANTIATE_D(64)
+FA_DEC_INSTANTIATE_D(96)
+FA_DEC_INSTANTIATE_D(128)
+#undef FA_DEC_INSTANTIATE_D
 #undef FA_DEC_INSTANTIATE
 
 template <typename T, int D>
@@ -305,11 +310,22 @@ hipError_t run_decode(const DecodeArgs& a) {
 
 }  // namespace dec
 
+namespace dec {
+template <typename T>
+hipError_t dispatch_dim(const DecodeArgs& a) {
+  switch (a.d) {
+    case 32: return run_decode<T, 32>(a);
+    case 64: return run_decode<T, 64>(a);
+    case 96: return run_decode<T, 96>(a);
+    default: return run_decode<T, 128>(a);
+  }
+}
+}  // namespace dec
+
 hipError_t launch_decode(const DecodeArgs& a) {
-  using namespace dec;
-  if (a.dtype == 0) return a.d == 64 ? run_decode<float, 64>(a) : run_decode<float, 128>(a);
-  if (a.dtype == 1) return a.d == 64 ? run_decode<_Float16, 64>(a) : run_decode<_Float16, 128>(a);
-  return a.d == 64 ? run_decode<__bf16, 64>(a) : run_decode<__bf16, 128>(a);
+  if (a.dtype == 0) return dec::dispatch_dim<float>(a);
+  if (a.dtype == 1) return dec::dispatch_dim<_Float16>(a);
+  return dec::dispatch_dim<__bf16>(a);
 }
 
 }  // namespace fa

@@ -164,20 +164,26 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 // XOR swizzle of the 16-byte chunks of an LDS tile row (r = tile row,
-// CPR = 16-byte chunks per row: 8 for d = 64, 16 for d = 128).  Element
-// (r, c) of a [rows][D] tile lives at r*D + ((c/8) ^ swz(r))*8 + c%8.  The
-// permutation makes both read patterns of a tile conflict-free on the 64
-// LDS banks: the row-wise 16-byte reads of 16 consecutive rows (one chunk
-// column) and the transpose reads of 4 consecutive rows x 4 chunks.
+// CPR = 16-byte chunks per row: 4, 8, 12, 16 for d = 32, 64, 96, 128).
+// Element (r, c) of a [rows][D] tile lives at r*D + ((c/8) ^ swz(r))*8 + c%8.
+// The permutation makes both read patterns of a tile conflict-free on the
+// 64 LDS banks (16 chunk-wide bank groups): the row-wise 16-byte reads of 16
+// consecutive rows (one chunk column) and the transpose reads of 4
+// consecutive rows x an aligned group of 4 chunks.  For 4- and 12-chunk rows
+// the 4 rows r, r+4, r+8, r+12 share a bank group, and swz = (r/4) mod 4
+// (below 4, so a chunk stays inside its aligned group of 4) separates them;
+// 4 consecutive rows then already fall in 4 different bank groups.
 template <int CPR>
-__device__ __forceinline__ int swz(int r) {
+__host__ __device__ __forceinline__ int swz(int r) {
+  static_assert(CPR == 4 || CPR == 8 || CPR == 12 || CPR == 16, "d must be 32, 64, 96 or 128");
   if (CPR == 8)  // bit-reversed (r >> 1) & 7
     return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
-  return ((r & 3) << 2) | ((r >> 2) & 3);
+  if (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (r >> 2) & 3;
 }
 
 template <int D>
-__device__ __forceinline__ int tile_off(int r, int c) {
+__host__ __device__ __forceinline__ int tile_off(int r, int c) {
   return r * D + (((c >> 3) ^ swz<D / 8>(r)) << 3) + (c & 7);
 }
 

@@ -29,6 +29,8 @@
 // is how the first tile of every row enters it).  Between rescalings the
 // output, l and m stay consistent, so the result is the same softmax up to
 // rounding; per-tile maxima are not needed on the common path.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -72,7 +74,7 @@ __device__ __forceinline__ int valid_keys(const int32_t* key_len, int b, int N) 
 
 template <int D>
 struct FwdShape {
-  static constexpr int QW = D == 64 ? FA_FWD_QW64 : 32;  // queries per wave
+  static constexpr int QW = D <= 64 ? FA_FWD_QW64 : 32;  // queries per wave
   static constexpr int NQB = QW / 32;           // 32-query MFMA blocks per wave
   static constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;             // 32-row blocks of O^T
@@ -511,15 +513,17 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParamsF32 p) {
   template __global__ void fwd_kernel<T, D, 4, true, false, true>(FwdParams);                \
   template __global__ void fwd_kernel<T, D, 4, false, false, true>(FwdParams);
 
-FA_FWD_INSTANTIATE(__bf16, 64)
-FA_FWD_INSTANTIATE(__bf16, 128)
-FA_FWD_INSTANTIATE(_Float16, 64)
-FA_FWD_INSTANTIATE(_Float16, 128)
+#define FA_FWD_INSTANTIATE_D(D)                                                               \
+  FA_FWD_INSTANTIATE(__bf16, D)                                                              \
+  FA_FWD_INSTANTIATE(_Float16, D)                                                            \
+  template __global__ void fwd_f32_kernel<D, true>(FwdParamsF32);                            \
+  template __global__ void fwd_f32_kernel<D, false>(FwdParamsF32);
+FA_FWD_INSTANTIATE_D(32)
+FA_FWD_INSTANTIATE_D(64)
+FA_FWD_INSTANTIATE_D(96)
+FA_FWD_INSTANTIATE_D(128)
+#undef FA_FWD_INSTANTIATE_D
 #undef FA_FWD_INSTANTIATE
-template __global__ void fwd_f32_kernel<64, true>(FwdParamsF32);
-template __global__ void fwd_f32_kernel<64, false>(FwdParamsF32);
-template __global__ void fwd_f32_kernel<128, true>(FwdParamsF32);
-template __global__ void fwd_f32_kernel<128, false>(FwdParamsF32);
 
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t run_fwd(const FwdArgs& a) {
@@ -571,10 +575,24 @@ hipError_t run_fwd_f32(const FwdArgs& a) {
 
 template <typename T, int D>
 hipError_t dispatch_mask(const FwdArgs& a) {
-  if (a.block_mask) return run_fwd<T, D, false, true, false>(a);
-  if (a.drop.on)
-    return a.causal ? run_fwd<T, D, true, false, true>(a) : run_fwd<T, D, false, false, true>(a);
-  return a.causal ? run_fwd<T, D, true, false, false>(a) : run_fwd<T, D, false, false, false>(a);
+  if constexpr (std::is_same<T, float>::value) {
+    return a.causal ? run_fwd_f32<D, true>(a) : run_fwd_f32<D, false>(a);
+  } else {
+    if (a.block_mask) return run_fwd<T, D, false, true, false>(a);
+    if (a.drop.on)
+      return a.causal ? run_fwd<T, D, true, false, true>(a) : run_fwd<T, D, false, false, true>(a);
+    return a.causal ? run_fwd<T, D, true, false, false>(a) : run_fwd<T, D, false, false, false>(a);
+  }
+}
+
+template <typename T>
+hipError_t dispatch_dim(const FwdArgs& a) {
+  switch (a.d) {
+    case 32: return dispatch_mask<T, 32>(a);
+    case 64: return dispatch_mask<T, 64>(a);
+    case 96: return dispatch_mask<T, 96>(a);
+    default: return dispatch_mask<T, 128>(a);
+  }
 }
 
 }  // namespace fwd
@@ -582,12 +600,9 @@ hipError_t dispatch_mask(const FwdArgs& a) {
 using namespace fwd;
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.dtype == 0) {  // FA_F32
-    if (a.d == 64) return a.causal ? run_fwd_f32<64, true>(a) : run_fwd_f32<64, false>(a);
-    return a.causal ? run_fwd_f32<128, true>(a) : run_fwd_f32<128, false>(a);
-  }
-  if (a.dtype == 1) return a.d == 64 ? dispatch_mask<_Float16, 64>(a) : dispatch_mask<_Float16, 128>(a);
-  return a.d == 64 ? dispatch_mask<__bf16, 64>(a) : dispatch_mask<__bf16, 128>(a);
+  if (a.dtype == 0) return dispatch_dim<float>(a);  // FA_F32
+  if (a.dtype == 1) return dispatch_dim<_Float16>(a);
+  return dispatch_dim<__bf16>(a);
 }
 
 }  // namespace fa

@@ -103,7 +103,7 @@ def fwd(lib, **kw):
     (dict(q=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
     (dict(q=P + 8), -1),                          # misaligned
     (dict(B=0), -1), (dict(N=0), -1), (dict(H=-1), -1),
-    (dict(d=96), -2), (dict(d=32), -2),
+    (dict(d=48), -2), (dict(d=160), -2), (dict(d=16), -2),
     (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1), (dict(scale=0.0), -1),
     (dict(causal=2), -1), (dict(dtype=7), -1),
     (dict(B=1 << 16, H=1 << 16, N=1), -1),        # B*H too large
@@ -174,7 +174,7 @@ def stage(lib, st, **kw):
 
 @pytest.mark.parametrize("st,kw,status", [
     (0, {}, -1), (4, {}, -1), (-1, {}, -1),
-    (1, dict(ws=None), -1), (2, dict(d=96), -2), (3, dict(dtype=F32, bm=P), -2),
+    (1, dict(ws=None), -1), (2, dict(d=80), -2), (3, dict(dtype=F32, bm=P), -2),
     (2, dict(bm=P, causal=1), -1), (2, dict(bm=P, key_len=P), -1), (3, dict(bm=P, bs=64), -2),
     (1, dict(ws_bytes=8), -1),
 ])
@@ -203,7 +203,7 @@ def decode(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(lse=None), -1), (dict(ws=None), -1), (dict(k=P + 4), -1),
-    (dict(Nq=0), -1), (dict(Nk=0), -1), (dict(B=0), -1), (dict(d=96), -2),
+    (dict(Nq=0), -1), (dict(Nk=0), -1), (dict(B=0), -1), (dict(d=112), -2),
     (dict(scale=0.0), -1), (dict(dtype=9), -1), (dict(ws_bytes=16), -1),
     (dict(Nk=1 << 25, H=1, d=128), -1),           # k exceeds 2^31 elements
 ])
@@ -222,7 +222,7 @@ def fwd_drop(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(p=-0.1), -1), (dict(p=1.0), -1), (dict(p=float("nan")), -1), (dict(q=None), -1),
-    (dict(dtype=F32), -2), (dict(d=96), -2),
+    (dict(dtype=F32), -2), (dict(d=256), -2),
 ])
 def test_dropout_validation(lib, kw, status):
     assert fwd_drop(lib, **kw) == status

@@ -34,7 +34,7 @@ def run(x, dtype, **kw):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("mask", ["none", "causal", "pad"])
 def test_autograd_matches_oracle(dtype, d, mask):
     import torch

@@ -35,7 +35,7 @@ def run(fa, x, key_len=None):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("Nq,Nk", [(1, 1), (1, 100), (3, 257), (5, 1000), (1, 4096), (8, 2500)])
 def test_decode_shapes(fa, dtype, d, Nq, Nk):
     x = make_decode_inputs(2, 3, Nq, Nk, d, dtype, seed=Nq * 7919 + Nk)

@@ -66,7 +66,7 @@ def run(fa, x, dtype, p, seed, offset, causal=False, key_len=None):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("N", [64, 129, 300])
 @pytest.mark.parametrize("mask", ["none", "causal", "pad"])
 @pytest.mark.parametrize("p", [0.1, 0.5])

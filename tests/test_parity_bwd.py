@@ -43,7 +43,7 @@ def edge_inputs(dtype, N, d, B=2, H=3, seed=12):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("N", [1, 7, 64, 100, 129, 300])
 @pytest.mark.parametrize("mask", ["none", "causal", "pad", "causal_pad"])
 def test_bwd_shapes_and_masks(fa, dtype, d, N, mask):
@@ -104,7 +104,8 @@ def check_sampled(x, w, dq, dk, dv, causal=False, block_mask=None):
         assert_close(f"dv h={h}", dv[0, h, jj], rv, tol)
 
 
-@pytest.mark.parametrize("name", ["long_causal", "long_causal_d128"])
+@pytest.mark.parametrize("name", ["long_causal", "long_causal_d32", "long_causal_d96",
+                                  "long_causal_d128"])
 def test_bwd_long_causal_sampled(fa, name):
     w = WORKLOADS[name]
     x = make_inputs(w)

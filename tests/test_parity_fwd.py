@@ -37,7 +37,7 @@ def edge_inputs(dtype, N, d, B=2, H=3, seed=11):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("N", [1, 7, 64, 100, 129, 300])
 @pytest.mark.parametrize("mask", ["none", "causal", "pad", "causal_pad"])
 def test_fwd_shapes_and_masks(fa, dtype, d, N, mask):
@@ -88,7 +88,8 @@ def test_fwd_full_workloads(fa, name):
     assert_close("lse", lse, lse_ref, TOL[w.dtype])
 
 
-@pytest.mark.parametrize("name", ["long_causal", "long_causal_d128"])
+@pytest.mark.parametrize("name", ["long_causal", "long_causal_d32", "long_causal_d96",
+                                  "long_causal_d128"])
 def test_fwd_long_causal_sampled(fa, name):
     w = WORKLOADS[name]
     x = make_inputs(w)

@@ -64,6 +64,10 @@ WORKLOADS = {
                             sample_rows=256, sample_keys=64),
     "long_causal_d128": Workload("long_causal_d128", 1, 16, 16384, 128, "bf16", causal=True,
                                  seed=4, sample_rows=256, sample_keys=64),
+    "long_causal_d32": Workload("long_causal_d32", 1, 16, 16384, 32, "bf16", causal=True,
+                                seed=4, sample_rows=256, sample_keys=64),
+    "long_causal_d96": Workload("long_causal_d96", 1, 16, 16384, 96, "bf16", causal=True,
+                                seed=4, sample_rows=256, sample_keys=64),
     "block_sparse": Workload("block_sparse", 1, 8, 65536, 64, "bf16", block_sparse=True,
                              seed=5, sample_rows=256, sample_keys=64, sample_key_heads=1,
                              sample_key_blocks=8),
