@@ -26,6 +26,8 @@ Modules:
   tiled online-softmax method, used only to check the pages' exactness claim.
 * :mod:`oracle.bruteforce` — pure-Python loops with ``math.exp``/``math.fsum``
   for tiny shapes.
+* :mod:`oracle.closed_forms` — attention at q = 0 (uniform rows) from running
+  or per-block sums, exact at the full workload sizes.
 
 Every function here is pinned by ``tests/test_oracle.py`` (and the dropout
 functions by ``tests/test_oracle_dropout.py``) against closed forms,
@@ -43,6 +45,7 @@ from .attention import (  # noqa: F401
     attention_key_grads,
     online_softmax_attention,
 )
+from .closed_forms import q_zero_attention  # noqa: F401
 from .dropout import (  # noqa: F401
     attention_bwd_dropout,
     attention_fwd_dropout,

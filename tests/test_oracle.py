@@ -17,6 +17,7 @@ import pytest
 
 import oracle
 from oracle import bruteforce
+from oracle.closed_forms import q_zero_attention
 from oracle.attention import (allowed_mask, attention_bwd, attention_fwd,
                               attention_key_grads, attention_rows,
                               online_softmax_attention)
@@ -473,3 +474,32 @@ def test_decode_shape_fewer_queries_than_keys(key_len):
     Of, lf = attention_fwd(q, k, v, 0.35, key_len=kl)
     np.testing.assert_array_equal(O, Of[:, :, rows])
     np.testing.assert_array_equal(lse, lf[:, :, rows])
+
+
+# --------------------------------------------------------------------------
+# P8 at scale: the running-sum closed forms used for the full-size GPU checks
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mask", MASKS + [dict(causal=True, key_len=np.array([5, 0])),
+                                          dict(block_mask=(np.eye(9, k=1, dtype=np.uint8)
+                                                           + np.tri(9, k=-2, dtype=np.uint8))
+                                               * (np.arange(9) != 4)[:, None].astype(np.uint8),
+                                               block_size=128)])
+def test_q_zero_running_sum_forms_equal_the_definition(mask):
+    # the O(N d^2) forms in oracle/closed_forms.py (chunked running sums,
+    # per-block sums) against the materialising definition at q = 0, on a
+    # length with several chunks and a ragged last block
+    B, H, N, d = 2, 2, 1100, 5
+    k, v, dO = rnd((B, H, N, d), 60), rnd((B, H, N, d), 61), rnd((B, H, N, d), 62)
+    q = np.zeros((B, H, N, d))
+    kw = {key: val for key, val in mask.items() if key != "block_size"}
+    if "key_len" in kw and len(kw["key_len"]) != B:
+        kw["key_len"] = kw["key_len"][:B]
+    O, lse = attention_fwd(q, k, v, 0.3, **mask)
+    dq, dk, dv = attention_bwd(q, k, v, dO, 0.3, **mask)
+    cO, cl, cdq, cdk, cdv = q_zero_attention(k, v, dO, 0.3, **kw)
+    np.testing.assert_array_equal(np.isfinite(cl), np.isfinite(lse))
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(cl[fin], lse[fin], atol=1e-12)
+    for a, b_ in ((cO, O), (cdq, dq), (cdk, dk), (cdv, dv)):
+        np.testing.assert_allclose(a, b_, atol=1e-11)

@@ -44,7 +44,7 @@ def edge_inputs(dtype, N, d, B=2, H=3, seed=12):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [32, 64, 96, 128])
-@pytest.mark.parametrize("N", [1, 7, 64, 100, 129, 300])
+@pytest.mark.parametrize("N", [1, 7, 63, 64, 100, 127, 129, 300, 1000])
 @pytest.mark.parametrize("mask", ["none", "causal", "pad", "causal_pad"])
 def test_bwd_shapes_and_masks(fa, dtype, d, N, mask):
     x = edge_inputs(dtype, N, d)
