@@ -248,6 +248,16 @@ __device__ inline uint32_t quad_or(uint32_t v) {
   return v;
 }
 
+// a ^ b ^ c; on the device one v_bitop3_b32 (gfx950's three-input bitwise
+// operation, 0x96 being the truth table of the three-way xor)
+__host__ __device__ inline uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+#else
+  return a ^ b ^ c;
+#endif
+}
+
 // Philox4x32-10, the counter-based generator of J. K. Salmon, M. A. Moraes,
 // R. O. Dror and D. E. Shaw ("Parallel random numbers: as easy as 1, 2,
 // 3", SC 2011): ten rounds, each multiplying counter words 0 and 2 by the
@@ -264,7 +274,8 @@ __host__ __device__ inline void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
       k1 += 0xBB67AE85u;
     }
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+    const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
