@@ -8,14 +8,16 @@
 // or a few queries there is too little work per head to fill the GPU with
 // query tiles, and the cost is reading K and V from HBM once.  The keys of
 // each head are therefore cut into chunks, one workgroup per (chunk, head,
-// group of 4 queries), and every workgroup leaves a partial result (m, l, O)
+// group of 4 queries, or the single query when there is one), and every
+// workgroup leaves a partial result (m, l, O)
 // for its chunk; a second launch merges a query's partials by rescaling
 // them to the common maximum — the same rescaling the online softmax does
 // between key tiles.
 //
 // Partial kernel: a key row of d values is read by d/8 lanes, 16 bytes each
 // (8 keys per wave and step at d = 64, 4 at d = 128), coalesced across the
-// wave.  Per key and query the lanes reduce q.k with shuffles; each lane
+// wave.  Per key and query the lanes reduce q.k with DPP moves inside their
+// row of lanes (no LDS round trip); each lane
 // keeps its own running (m, l, O-slice) in base 2 for the keys it sees.
 // The key slots of a wave are merged with shuffles, the 4 waves through
 // LDS.  The work is HBM-bound: about 4 d bytes of K and V per key against
@@ -27,7 +29,27 @@ namespace fa {
 
 namespace dec {
 
-constexpr int kQG = 4;  // queries per workgroup
+constexpr int kQG = 4;  // queries per workgroup when there are several
+
+// x of the lane that DPP control CTRL selects (every lane of the wave active)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum of x over each aligned group of G lanes (G = 4, 8, 16), in every lane
+// of the group: quad swaps [1,0,3,2] and [2,3,0,1], then lane i <- 7 - i
+// inside 8 lanes (row_half_mirror) and lane i <- 15 - i inside 16
+// (row_mirror), each one DPP move.
+template <int G>
+__device__ __forceinline__ float group_sum_dpp(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  if constexpr (G >= 8) x += dpp_mov<0x141>(x);
+  if constexpr (G >= 16) x += dpp_mov<0x140>(x);
+  return x;
+}
 
 struct DecodeParams {
   const uint16_t* q;  // element type T (fp32 is read as two 16-byte halves)
@@ -93,22 +115,22 @@ __device__ __forceinline__ float rel_exp2(float a, float b) {
   return a == neg_inf() ? 0.f : fast_exp2(a - b);
 }
 
-// grid: x = chunk + nchunks * bh, y = query group; 256 threads
-template <typename T, int D>
+// grid: x = chunk + nchunks * bh, y = query group of QG queries; 256 threads
+template <typename T, int D, int QG>
 __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   // lanes per key row: one per 8 elements, rounded up to a power of two for
   // the shuffle reductions (d = 96: 16 lanes, the last 4 hold no elements)
   constexpr int LPK = D / 8 <= 4 ? 4 : D / 8 <= 8 ? 8 : 16;
   constexpr int KPW = 64 / LPK;   // keys per wave and step
   constexpr int EB = Ld<T>::ES;   // bytes per element
-  __shared__ float sm[4][kQG], sl[4][kQG];
-  __shared__ float sO[4][kQG][D];
+  __shared__ float sm[4][QG], sl[4][QG];
+  __shared__ float sO[4][QG][D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int chunk = blockIdx.x % p.nchunks, bh = blockIdx.x / p.nchunks;
-  const int q0 = blockIdx.y * kQG;
-  const int nq = p.Nq - q0 < kQG ? p.Nq - q0 : kQG;
+  const int q0 = blockIdx.y * QG;
+  const int nq = p.Nq - q0 < QG ? p.Nq - q0 : QG;
   const int b = bh / p.H;
   int L = p.Nk;
   if (p.key_len) {
@@ -123,9 +145,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   const int ke = kb + wlen < L ? kb + wlen : L;
 
   // queries (scaled by c, base 2), this lane's d-slice
-  float qv[kQG][8];
+  float qv[QG][8];
 #pragma unroll
-  for (int i = 0; i < kQG; ++i) {
+  for (int i = 0; i < QG; ++i) {
     if (i < nq && dok) {
       const size_t off = (((size_t)bh * p.Nq + q0 + i) * D + dsl) * (EB / 2);
       load8<T>(p.q + off, qv[i]);
@@ -136,9 +158,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
       for (int e = 0; e < 8; ++e) qv[i][e] = 0.f;
     }
   }
-  float m[kQG], l[kQG], o[kQG][8];
+  float m[QG], l[QG], o[QG][8];
 #pragma unroll
-  for (int i = 0; i < kQG; ++i) {
+  for (int i = 0; i < QG; ++i) {
     m[i] = neg_inf();
     l[i] = 0.f;
 #pragma unroll
@@ -148,11 +170,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   const size_t kvbase = (size_t)bh * p.Nk * D;
   // U key steps per iteration: their K and V loads are issued together
   // before any of them is used, so that several 16-byte loads per lane are
-  // in flight (the loop holds shuffles, which the compiler does not unroll)
+  // in flight (the loop holds cross-lane moves, which the compiler does not
+  // unroll).  16-bit data: 16 steps (32 loads in flight per lane, about 160
+  // registers; measured 2-3 % above 4 or 8 steps); fp32 takes two loads per
+  // step and keeps 4 (16 steps would need over 256 registers).
 #ifndef FA_DEC_STEPS
-#define FA_DEC_STEPS 4
+#define FA_DEC_STEPS 16
 #endif
-  constexpr int U = FA_DEC_STEPS;
+  constexpr int U = Ld<T>::ES == 4 ? 4 : FA_DEC_STEPS;
   constexpr int NR = Ld<T>::NR;
   for (int k0 = kb; k0 < ke; k0 += KPW * U) {
     u32x4 kr[U][NR], vr[U][NR];
@@ -176,12 +201,11 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
       Ld<T>::widen(kr[u], kf);
       Ld<T>::widen(vr[u], vf);
 #pragma unroll
-      for (int i = 0; i < kQG; ++i) {
+      for (int i = 0; i < QG; ++i) {
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) s = fmaf(qv[i][e], kf[e], s);
-#pragma unroll
-        for (int off = 1; off < LPK; off <<= 1) s += __shfl_xor(s, off);
+        s = group_sum_dpp<LPK>(s);
         s = ok[u] ? s : neg_inf();
         const float mn = fmaxf(m[i], s);
         const float alpha = rel_exp2(m[i], mn);
@@ -198,7 +222,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
   for (int off = LPK; off < 64; off <<= 1) {
 #pragma unroll
-    for (int i = 0; i < kQG; ++i) {
+    for (int i = 0; i < QG; ++i) {
       const float mo = __shfl_xor(m[i], off), lo = __shfl_xor(l[i], off);
       const float mn = fmaxf(m[i], mo);
       const float a = rel_exp2(m[i], mn), bb = rel_exp2(mo, mn);
@@ -210,7 +234,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   }
   if (slot == 0) {
 #pragma unroll
-    for (int i = 0; i < kQG; ++i) {
+    for (int i = 0; i < QG; ++i) {
       if (dok)
 #pragma unroll
         for (int e = 0; e < 8; ++e) sO[wave][i][dsl + e] = o[i][e];
@@ -272,7 +296,8 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* part, uint
 }
 
 #define FA_DEC_INSTANTIATE(T, D)                                                  \
-  template __global__ void decode_partial_kernel<T, D>(DecodeParams);            \
+  template __global__ void decode_partial_kernel<T, D, 1>(DecodeParams);         \
+  template __global__ void decode_partial_kernel<T, D, kQG>(DecodeParams);       \
   template __global__ void decode_merge_kernel<T, D>(const float*, uint16_t*, float*, int);
 #define FA_DEC_INSTANTIATE_D(D) \
   FA_DEC_INSTANTIATE(__bf16, D) FA_DEC_INSTANTIATE(_Float16, D) FA_DEC_INSTANTIATE(float, D)
@@ -299,8 +324,12 @@ hipError_t run_decode(const DecodeArgs& a) {
   p.chunk = sp.chunk;
   p.c = a.scale * kLog2e;
   p.key_len = a.key_len;
+  // one query: a group of one (no idle query slots in the inner loop)
   const dim3 grid((unsigned)(sp.nchunks * p.BH), (unsigned)((a.Nq + kQG - 1) / kQG));
-  hipLaunchKernelGGL((decode_partial_kernel<T, D>), grid, dim3(256), 0, a.stream, p);
+  if (a.Nq == 1)
+    hipLaunchKernelGGL((decode_partial_kernel<T, D, 1>), grid, dim3(256), 0, a.stream, p);
+  else
+    hipLaunchKernelGGL((decode_partial_kernel<T, D, kQG>), grid, dim3(256), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(p.BH * a.Nq)), dim3(D), 0,
