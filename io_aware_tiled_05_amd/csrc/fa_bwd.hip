@@ -294,18 +294,6 @@ struct BwdParams {
   int nblk;
 };
 
-// x as hi + mid + lo bf16 parts (24 significant bits); non-finite x goes
-// entirely into hi.
-__device__ __forceinline__ void split3_bf16(float x, __bf16 out[3]) {
-  const __bf16 hi = (__bf16)x;
-  const bool fin = __builtin_isfinite(x);
-  const float r1 = fin ? x - (float)hi : 0.f;
-  const __bf16 mid = (__bf16)r1;
-  out[0] = hi;
-  out[1] = mid;
-  out[2] = (__bf16)(r1 - (float)mid);
-}
-
 // B operand (P or dS, 16 keys or queries of chunk a) from a 32x32
 // accumulator: chunk a covers accumulator elements 8(a%2) .. 8(a%2)+7 of
 // block a/2, i.e. rows 16a + 4h + 0..3 and 16a + 8 + 4h + 0..3.
@@ -597,13 +585,13 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
 // dQ: one workgroup per 128 queries, 32 per wave
 //
 // Scores run on fp16 operands (c Q 2^-eq against K 2^-ek, the fp16 copies
-// of the convert pass) and dP on the input type.  Each product gets one
-// more k-step whose A operand is a constant column of ones and whose B
-// operand carries the query's -shift 2^-f (scores) or -D (dP) split into
-// three bf16 parts, so the accumulators end as the exponent of P and as
-// dP - D: P is one exponential and dS one multiply.
+// of the convert pass) and dP on the input type.  The first k-step of each
+// product starts from the query's -shift 2^-f (scores) or -D (dP) as its C
+// operand, so the accumulators end as the exponent of P and as dP - D: P is
+// one exponential and dS one multiply.
 // ---------------------------------------------------------------------------
-// DROP: dS = P (dP M / (1 - p) - D); the -D k-step is left out
+// DROP: dS = P (dP M / (1 - p) - D); dP starts from 0 and D enters after
+// the mask
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32, TILE = kBC * D, NW = 4;
@@ -642,22 +630,19 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
     qf[ks] = as_vec8<TI>(ldg16(p.q16 + base + (size_t)query * D + ks * 16 + h * 8, qok));
     of[ks] = as_vec8<T>(ldg16(p.dO + base + (size_t)query * D + ks * 16 + h * 8, qok));
   }
-  // the extra k-step (a bf16 MFMA into the same fp32 accumulators, so any
-  // magnitude fits): A = 1 in k-slots 0..2 (lanes h = 0), B = the row value
-  // split into three bf16 parts there (24 significant bits), zero elsewhere
-  bf16x8 one_b, s_aug_b, d_aug_b;
+  // the row terms of this lane's query (-shift 2^-f for the scores, -D for
+  // dP; dropout subtracts D after the mask instead), replicated: every
+  // element of a lane's 32 x 32 accumulator block belongs to its query, so
+  // the first k-step of each product takes them as its C operand and the
+  // fp32 accumulator starts from them exactly
+  f32x16 s_init, dp_init;
   {
     const float ns = qok ? p.nsh[(size_t)bh * N + query] : neg_inf();
-    const float nd = qok ? -p.Dbuf[(size_t)bh * N + query] : 0.f;
-    __bf16 sp[3], dq3[3];
-    split3_bf16(ns, sp);
-    split3_bf16(nd, dq3);
+    const float nd = qok && !DROP ? -p.Dbuf[(size_t)bh * N + query] : 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool slot = h == 0 && j < 3;
-      one_b[j] = slot ? (__bf16)1.f : (__bf16)0.f;
-      s_aug_b[j] = slot ? sp[j < 3 ? j : 0] : (__bf16)0.f;
-      d_aug_b[j] = slot ? dq3[j < 3 ? j : 0] : (__bf16)0.f;
+    for (int e = 0; e < 16; ++e) {
+      s_init[e] = ns;
+      dp_init[e] = nd;
     }
   }
   f32x16 acc[DB];  // dQ^T: rows d = 32db + 8i + 4h + j, column = query
@@ -690,20 +675,13 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
     }
     f32x16 s[2], dp[2];  // rows = keys 32 kb + 8i + 4h + j, column = query
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = dp[kb][e] = 0.f;
-      s[kb] = Elt<__bf16>::mfma32(one_b, s_aug_b, s[kb]);
-      if constexpr (!DROP) dp[kb] = Elt<__bf16>::mfma32(one_b, d_aug_b, dp[kb]);
-    }
-#pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const hvec8 ak = as_vec8<TI>(lds16(tk + roff[ks] + kb * 32 * D));
         const vec8 av = as_vec8<T>(lds16(tv + roff[ks] + kb * 32 * D));
-        s[kb] = Elt<TI>::mfma32(ak, qf[ks], s[kb]);
-        dp[kb] = Elt<T>::mfma32(av, of[ks], dp[kb]);
+        s[kb] = Elt<TI>::mfma32(ak, qf[ks], ks == 0 ? s_init : s[kb]);
+        dp[kb] = Elt<T>::mfma32(av, of[ks], ks == 0 ? dp_init : dp[kb]);
       }
     prefetch();
     const bool need_mask = (kt0 + kBC > L) || (CAUSAL && kt0 + kBC - 1 > qw);
