@@ -157,10 +157,12 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v,
 /* Forward with dropout on the probabilities ([HFL] "Standard Attention
  * Algorithm" names dropout, with masking and softmax, among the elementwise
  * passes that dominate standard attention; here it is fused into the
- * kernel): O = (P * M / (1 - p)) v with M_ij kept iff word j mod 4 of
+ * kernel): O = (P * M / (1 - p)) v with M_ij kept iff 16-bit draw t(j) of
  * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011) at counter
- * (j / 4, i, b*H + h, offset) and key (seed mod 2^32, seed / 2^32) is >=
- * floor(p 2^32).  lse is that of P (the un-dropped softmax).  The mask
+ * (g(j), i, b*H + h, offset) and key (seed mod 2^32, seed / 2^32) is >=
+ * floor(p 2^16), where g(j) = 2 (j / 16) + (j / 4) mod 2,
+ * t(j) = 4 ((j / 8) mod 2) + j mod 4, and draw t is half t mod 2 (low half
+ * first) of output word t / 2.  lse is that of P (the un-dropped softmax).  The mask
  * depends only on (seed, offset) and the element's indices, so fa_bwd_dropout
  * regenerates it instead of storing it.  Other arguments as fa_fwd.
  *   dropout_p : in [0, 1); 0 gives fa_fwd's result.  Outside: FA_ERR_INVALID

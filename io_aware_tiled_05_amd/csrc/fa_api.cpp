@@ -43,8 +43,8 @@ int make_dropout(float p, uint64_t seed, uint32_t offset, fa::Dropout* out) {
   if (!std::isfinite(p) || p < 0.f || p >= 1.f) return FA_ERR_INVALID;
   fa::Dropout dr;
   dr.on = p > 0.f;
-  const double t = std::floor((double)p * 4294967296.0);
-  dr.thresh = t >= 4294967295.0 ? 4294967295u : (uint32_t)t;
+  const double t = std::floor((double)p * 65536.0);  // 16-bit draws
+  dr.thresh = t >= 65535.0 ? 65535u : (uint32_t)t;
   dr.rinv = (float)(1.0 / (1.0 - (double)p));
   dr.k0 = (uint32_t)(seed & 0xFFFFFFFFu);
   dr.k1 = (uint32_t)(seed >> 32);

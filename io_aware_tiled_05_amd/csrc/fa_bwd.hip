@@ -444,36 +444,46 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
     // selects: query q0 + 32qb + 4h + o, o = 8(e/4) + e%4, sees this lane's
     // key iff lo <= o < hi.
     if constexpr (DROP) {
-      // Element e is query q0 + 32qb + 8(e/4) + 4h + e%4 of this lane's key:
-      // word key % 4 of the counter (key / 4, query).  The four lanes of a
-      // quad hold keys 4m .. 4m + 3 and the same four queries of each
-      // (qb, e/4) block, so lane t draws the counter of the block's query t
-      // (its four words are the four keys' draws), turns them into four
-      // keep bits, and the quad exchanges the bits: bit 4j + t of the OR is
-      // key 4m + t at query j.  One generator call per four elements.
-      const int t = lane & 3;
+      // Element e is query q0 + 32qb + 8(e/4) + 4h + e%4 of this lane's key.
+      // One generator call covers 8 keys at one query: the keys of this
+      // lane's call group are held by the 8 lanes that differ from it in
+      // lane bits 0, 1, 3, and this lane's key is draw t8 of the call.  For
+      // the 8 queries of a pair of element rows (e/4 = 2c, 2c+1), the lane at
+      // position t8 draws the call of query t8 and turns its 8 draws into
+      // a byte of keep bits (bit t: the key of draw t); the 8 lanes gather
+      // the bytes into 64 bits (byte u: query u), and each lane reads bit
+      // t8 of every byte.  One call per 8 elements.
+      const int t8 = (lane & 3) | ((lane >> 1) & 4);
+      const uint32_t gk = (uint32_t)drop_call(key), th = p.drop.thresh;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int qbase = q0 + qb * 32 + 4 * h;
         const int hi = key < L ? N - qbase : -64;
         const int lo = CAUSAL ? key - qbase : -64;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 nd4 = *reinterpret_cast<const f32x4*>(td + qb * 32 + 8 * i + 4 * h);
+        for (int c2 = 0; c2 < 2; ++c2) {
           uint32_t w[4];
-          philox4x32_10((uint32_t)key >> 2, (uint32_t)(qbase + 8 * i + t), (uint32_t)bh,
-                        p.drop.offset, p.drop.k0, p.drop.k1, w);
-          const uint32_t th = p.drop.thresh;
-          const uint32_t nib = (w[0] >= th ? 1u : 0u) | (w[1] >= th ? 2u : 0u) |
-                               (w[2] >= th ? 4u : 0u) | (w[3] >= th ? 8u : 0u);
-          const uint32_t bits = quad_or(nib << (4 * t)) >> t;
+          philox4x32_10(gk, (uint32_t)(qbase + 8 * (2 * c2 + (t8 >> 2)) + (t8 & 3)),
+                        (uint32_t)bh, p.drop.offset, p.drop.k0, p.drop.k1, w);
+          uint32_t byte = 0u;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int o = 8 * i + j, e = 4 * i + j;
-            const float pv = ((o >= lo) & (o < hi)) ? fast_exp2(s[qb][e]) : 0.f;
-            const float mk = (bits >> (4 * j)) & 1u ? p.drop.rinv : 0.f;
-            dp[qb][e] = pv * fmaf(mk, dp[qb][e], nd4[j]);
-            s[qb][e] = pv * mk;
+          for (int u = 0; u < 4; ++u)
+            byte |= (((w[u] & 0xFFFFu) >= th ? 1u : 0u) | (w[u] >= (th << 16) ? 2u : 0u))
+                    << (2 * u);
+          const uint32_t xlo = or8_bits013(t8 < 4 ? byte << (8 * t8) : 0u) >> t8;
+          const uint32_t xhi = or8_bits013(t8 >= 4 ? byte << (8 * (t8 - 4)) : 0u) >> t8;
+#pragma unroll
+          for (int il = 0; il < 2; ++il) {
+            const int i = 2 * c2 + il;
+            const f32x4 nd4 = *reinterpret_cast<const f32x4*>(td + qb * 32 + 8 * i + 4 * h);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int o = 8 * i + j, e = 4 * i + j;
+              const float pv = ((o >= lo) & (o < hi)) ? fast_exp2(s[qb][e]) : 0.f;
+              const float mk = ((il ? xhi : xlo) >> (8 * j)) & 1u ? p.drop.rinv : 0.f;
+              dp[qb][e] = pv * fmaf(mk, dp[qb][e], nd4[j]);
+              s[qb][e] = pv * mk;
+            }
           }
         }
       }
@@ -698,17 +708,23 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
         const int kbase = kt0 + kb * 32 + 4 * h;
         int thr = L - 1 - kbase;
         if (CAUSAL) thr = min(thr, query - kbase);
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          // elements 4i .. 4i+3: keys kbase + 8i + 0..3, one counter
-          uint32_t w[4];
-          philox4x32_10((uint32_t)(kbase + 8 * i) >> 2, (uint32_t)query, (uint32_t)bh,
-                        p.drop.offset, p.drop.k0, p.drop.k1, w);
+          // elements 8c .. 8c+7 (i = 2c, 2c+1): keys kbase + 16c + {0..3,
+          // 8..11}, one generator call; element 4i + j takes the low (j
+          // even) or high half of word 2 (i % 2) + j / 2
+          if ((i & 1) == 0)
+            philox4x32_10((uint32_t)drop_call(kbase + 8 * i), (uint32_t)query, (uint32_t)bh,
+                          p.drop.offset, p.drop.k0, p.drop.k1, w);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int e = 4 * i + j;
+            const uint32_t wd = w[2 * (i & 1) + (j >> 1)];
+            const bool keep = (j & 1) ? wd >= (p.drop.thresh << 16)
+                                      : (wd & 0xFFFFu) >= p.drop.thresh;
             const float pv = 8 * i + j <= thr ? fast_exp2(s[kb][e]) : 0.f;
-            const float mk = w[j] >= p.drop.thresh ? p.drop.rinv : 0.f;
+            const float mk = keep ? p.drop.rinv : 0.f;
             dp[kb][e] = pv * fmaf(mk, dp[kb][e], -dq_D);
           }
         }

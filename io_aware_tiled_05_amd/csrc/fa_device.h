@@ -248,6 +248,15 @@ __device__ inline uint32_t quad_or(uint32_t v) {
   return v;
 }
 
+// OR of v over the 8 lanes that differ from this one in lane bits 0, 1 and
+// 3 (inside one row of 16): the two quad swaps, then row_ror:8, which
+// brings lane i ^ 8 of the row.  Every lane of the wave must be active.
+__device__ inline uint32_t or8_bits013(uint32_t v) {
+  v = quad_or(v);
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  return v;
+}
+
 // a ^ b ^ c; on the device one v_bitop3_b32 (gfx950's three-input bitwise
 // operation, 0x96 being the truth table of the three-way xor)
 __host__ __device__ inline uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {

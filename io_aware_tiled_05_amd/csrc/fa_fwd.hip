@@ -209,22 +209,24 @@ __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(Fwd
         float r[4] = {0.f, 0.f, 0.f, 0.f};  // four independent sum chains
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};  // dropout words of the current 4 keys
+          uint32_t w[4] = {0u, 0u, 0u, 0u};  // dropout draws of the current 8 keys
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             float x0 = fast_exp2(fmaf(s[kb][qb][2 * e], c, -msc));
             float x1 = fast_exp2(fmaf(s[kb][qb][2 * e + 1], c, -msc));
             if constexpr (DROP) {
-              // elements 4i .. 4i+3 are keys kt0 + 32 kb + 8i + 4h + 0..3
-              if ((e & 1) == 0)
-                philox4x32_10((uint32_t)(kt0 + kb * 32 + 8 * (e >> 1) + 4 * h) >> 2,
+              // elements 8c .. 8c+7 (pairs e = 4c .. 4c+3) are keys
+              // kt0 + 32 kb + 16 c + 4 h + {0..3, 8..11}: one generator call;
+              // pair e takes word e % 4, low half for x0 and high for x1
+              if ((e & 3) == 0)
+                philox4x32_10((uint32_t)drop_call(kt0 + kb * 32 + 16 * (e >> 2) + 4 * h),
                               (uint32_t)(qw + qb * 32 + l32), (uint32_t)bh, p.drop.offset,
                               p.drop.k0, p.drop.k1, w);
               r[(2 * e) & 3] += x0;
               r[(2 * e + 1) & 3] += x1;
-              const int j = 2 * (e & 1);
-              x0 = w[j] >= p.drop.thresh ? x0 * p.drop.rinv : 0.f;
-              x1 = w[j + 1] >= p.drop.thresh ? x1 * p.drop.rinv : 0.f;
+              const uint32_t wd = w[e & 3];
+              x0 = (wd & 0xFFFFu) >= p.drop.thresh ? x0 * p.drop.rinv : 0.f;
+              x1 = wd >= (p.drop.thresh << 16) ? x1 * p.drop.rinv : 0.f;
               pk[kb][qb][e] = Elt<T>::pack2(x0, x1);
             } else {
               pk[kb][qb][e] = Elt<T>::pack2(x0, x1);

@@ -9,8 +9,13 @@
 namespace fa {
 
 // Dropout on the probabilities (off unless `on`): element (b, h, i, j) is
-// kept iff word j mod 4 of Philox4x32-10(counter = (j div 4, i, b H + h,
-// offset), key = (k0, k1)) is >= thresh; kept values are multiplied by rinv.
+// kept iff 16-bit draw t(j) of Philox4x32-10(counter = (g(j), i, b H + h,
+// offset), key = (k0, k1)) is >= thresh (< 2^16); kept values are
+// multiplied by rinv.  g(j) = 2 (j div 16) + (j div 4) mod 2 and
+// t(j) = 4 ((j div 8) mod 2) + j mod 4; draw t is the low (t even) or high
+// half of output word t div 2.  A lane of the kernels holds, for one query,
+// exactly the 8 keys of one call: keys 16 c + 4 h + {0..3, 8..11}.
+__host__ __device__ inline int drop_call(int j) { return 2 * (j >> 4) + ((j >> 2) & 1); }
 struct Dropout {
   int on = 0;
   uint32_t thresh = 0;

@@ -21,10 +21,20 @@ generator Philox4x32-10 (J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw,
 "Parallel random numbers: as easy as 1, 2, 3", SC 2011), written here from
 its published definition: each of 10 rounds multiplies counter words 0 and 2
 by 0xD2511F53 and 0xCD9E8D57 into 64-bit products and forms the new counter
-(hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key words are increased by
-0x9E3779B9 and 0xBB67AE85 between rounds.  Element (b, h, i, j) takes word
-j mod 4 of Philox(counter = (j div 4, i, b H + h, offset), key = (seed mod
-2^32, seed div 2^32)) and is kept iff that word is >= floor(p 2^32).
+(hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key is increased by
+0x9E3779B9 and 0xBB67AE85 between rounds.  One call gives four 32-bit words,
+read as eight 16-bit draws (half u of word w is draw 2 w + u, low half
+first).  The keys are taken 16 at a time; inside a block of 16, the 8 keys
+with bit 2 of j clear share one call and the 8 with it set another:
+
+    call  g(j) = 2 (j div 16) + (j div 4) mod 2
+    draw  t(j) = 4 ((j div 8) mod 2) + j mod 4
+
+Element (b, h, i, j) takes draw t(j) of Philox(counter = (g(j), i, b H + h,
+offset), key = (seed mod 2^32, seed div 2^32)) and is kept iff that draw is
+>= floor(p 2^16), so the keep probability is 1 - p to within 2^-16.  (The
+grouping follows the register layout of the kernels, where a lane holds
+exactly those 8 keys of one query; the pages fix no generator.)
 """
 
 from __future__ import annotations
@@ -33,8 +43,8 @@ import numpy as np
 
 from .attention import _f64, _key_len_of, _row_softmax, _visible, allowed_mask
 
-__all__ = ["philox4x32_10", "drop_threshold", "keep_mask", "attention_fwd_dropout",
-           "attention_bwd_dropout"]
+__all__ = ["philox4x32_10", "drop_threshold", "draw_index", "keep_mask",
+           "attention_fwd_dropout", "attention_bwd_dropout"]
 
 _M0, _M1 = np.uint64(0xD2511F53), np.uint64(0xCD9E8D57)
 _W0, _W1 = np.uint64(0x9E3779B9), np.uint64(0xBB67AE85)
@@ -61,19 +71,28 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
 
 
 def drop_threshold(p: float) -> int:
-    """Words below this are dropped: floor(p 2^32), at most 2^32 - 1."""
-    return min(int(np.floor(float(p) * 4294967296.0)), 4294967295)
+    """Draws below this are dropped: floor(p 2^16), at most 2^16 - 1."""
+    return min(int(np.floor(float(p) * 65536.0)), 65535)
+
+
+def draw_index(j):
+    """(call g, draw t) of key j (module docstring)."""
+    j = np.asarray(j, dtype=np.int64)
+    return 2 * (j // 16) + (j // 4) % 2, 4 * ((j // 8) % 2) + j % 4
 
 
 def keep_mask(rows, n_keys, bh, p, seed, offset=0):
     """bool [len(rows), n_keys]: entry (r, j) kept for query rows[r], key j
     of head index bh = b H + h."""
     rows = np.asarray(rows, dtype=np.uint64)
-    groups = np.arange((n_keys + 3) // 4, dtype=np.uint64)
-    words = philox4x32_10(groups[None, :], rows[:, None], bh, offset,
+    g, t = draw_index(np.arange(n_keys))
+    calls = np.arange(int(g.max()) + 1 if n_keys else 0, dtype=np.uint64)
+    words = philox4x32_10(calls[None, :], rows[:, None], bh, offset,
                           int(seed) & 0xFFFFFFFF, int(seed) >> 32)
-    w = np.stack(words, axis=-1).reshape(rows.size, -1)[:, :n_keys]
-    return w >= np.uint64(drop_threshold(p))
+    w = np.stack(words, axis=-1)                      # [rows, calls, 4]
+    draws = np.stack([w & np.uint64(0xFFFF), w >> np.uint64(16)], axis=-1)
+    draws = draws.reshape(rows.size, calls.size, 8)   # draw 2 w + u
+    return draws[:, g, t] >= np.uint64(drop_threshold(p))
 
 
 def attention_fwd_dropout(q, k, v, scale, p, seed, offset=0, causal=False, key_len=None,

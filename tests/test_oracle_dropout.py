@@ -9,6 +9,9 @@
 * The mask: kept fraction within binomial bounds of 1 - p, different
   seeds / offsets / heads give different masks, and averaging O over many
   masks approaches the dropout-free O (the 1/(1 - p) scaling).
+* The draw map: every (call, draw) pair of a 16-key block is used exactly
+  once, and the vectorised mask agrees element by element with a scalar
+  reading of one generator call per element.
 """
 
 import numpy as np
@@ -16,6 +19,7 @@ import pytest
 
 from oracle import (attention_bwd, attention_bwd_dropout, attention_fwd, attention_fwd_dropout,
                     drop_threshold, keep_mask, philox4x32_10)
+from oracle.dropout import draw_index
 
 
 def test_philox_known_answers():
@@ -103,8 +107,8 @@ def test_mask_statistics_and_independence():
     n = m.size
     kept = m.mean()
     assert abs(kept - (1 - p)) < 5 * np.sqrt(p * (1 - p) / n)
-    assert drop_threshold(p) == int(np.floor(0.3 * 2 ** 32))
-    assert drop_threshold(0.0) == 0
+    assert drop_threshold(p) == int(np.floor(0.3 * 2 ** 16))
+    assert drop_threshold(0.0) == 0 and drop_threshold(0.999999) == 65535
     # every other index changes the mask
     for other in (keep_mask(np.arange(512), 512, 3, p, seed=2025),
                   keep_mask(np.arange(512), 512, 3, p, seed=2024, offset=1),
@@ -125,3 +129,29 @@ def test_mean_over_masks_is_the_dropout_free_output():
     # each entry is a mean of n draws with std <= max|v| / sqrt(n) * sqrt(p/(1-p))
     tol = 5 * np.abs(v).max() * np.sqrt(p / (1 - p) / n)
     np.testing.assert_allclose(acc / n, O0, rtol=0, atol=tol)
+
+
+def test_draw_map_is_a_bijection_per_16_keys():
+    g, t = draw_index(np.arange(16 * 7))
+    pairs = set(zip(g.tolist(), t.tolist()))
+    assert len(pairs) == 16 * 7                          # no (call, draw) used twice
+    assert set(g.tolist()) == set(range(14)) and set(t.tolist()) == set(range(8))
+    # the 8 keys of a call: one 16-key block, one value of bit 2
+    for call in range(14):
+        js = np.nonzero(g == call)[0]
+        assert len(js) == 8 and len(set((js // 16).tolist())) == 1
+        assert len(set(((js >> 2) & 1).tolist())) == 1
+
+
+def test_mask_matches_one_call_per_element():
+    p, seed, off, bh = 0.37, (0xDEADBEEF << 32) | 0x12345, 5, 6
+    rows, nk = np.array([0, 3, 1000]), 45
+    m = keep_mask(rows, nk, bh, p, seed, off)
+    th = drop_threshold(p)
+    for r, i in enumerate(rows):
+        for j in range(nk):
+            g, t = (int(x) for x in draw_index(j))
+            w = philox4x32_10(g, int(i), bh, off, seed & 0xFFFFFFFF, seed >> 32)
+            word = int(w[t // 2])
+            draw = (word >> 16) if t % 2 else (word & 0xFFFF)
+            assert m[r, j] == (draw >= th), (i, j)
