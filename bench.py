@@ -26,6 +26,15 @@ cache: B=16, H=16, d=64, bf16) and reports the rate at which it streams K
 and V, against MI355X's 8 TB/s HBM: the decode reads each cached key and
 value once and does 4 d flops per key, so it is bound by HBM, not MFMA.
 
+    python bench.py --sweep [--steps K] [--warmup W]
+
+prints one line per point of the sequence-length sweep: H = 16, B = 16384/N,
+N = 1K, 2K, 4K, 8K, 16K, d = 64, bf16, causal and non-causal (the same
+total tokens at every length).  Any workload of ``workloads.WORKLOADS`` can
+be timed with --workload, including key padding (bert_large) and the
+block-sparse one; the FLOP count is 4 d (forward) + 10 d (backward) per
+visible (query, key) pair, counted exactly under each mask.
+
     python bench.py --dropout P [--steps K] [--warmup W]
 
 times the same step with dropout at rate P (fa_fwd_dropout, fa_bwd_dropout;
@@ -61,10 +70,20 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def pairs_of(w, N=None):
-    N = w.N if N is None else N
-    per_head = N * (N + 1) // 2 if w.causal else N * N
-    return w.B * w.H * per_head
+def visible_pairs(w, x):
+    """Visible (query, key) pairs of the whole batch: causal, key padding
+    (keys j < key_len[b]) and 128 x 128 block masks counted exactly."""
+    import numpy as np
+    N = w.N
+    if w.block_sparse:
+        bm = np.asarray(x["block_mask"], dtype=np.int64)
+        size = np.minimum(128, N - 128 * np.arange(bm.shape[0])).astype(np.int64)
+        return w.B * w.H * int(size @ bm @ size)
+    lens = [N] * w.B if x["key_len"] is None else [min(max(int(v), 0), N) for v in x["key_len"]]
+    total = 0
+    for L in lens:  # causal: query i sees min(i + 1, L) keys
+        total += L * (L + 1) // 2 + (N - L) * L if w.causal else N * L
+    return w.H * total
 
 
 def measured_traffic(kernel: str):
@@ -210,56 +229,14 @@ def bench_decode(args, fa, torch, np):
     }), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="long_causal")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV",
-                    "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_MIB"),
-                    help="write profiles/hbm_traffic.json from rocprofv3 --pmc csv files and exit")
-    ap.add_argument("--decode", action="store_true",
-                    help="time fa_decode on the long-context decode shape instead")
-    ap.add_argument("--dropout", type=float, default=0.0,
-                    help="time the step with dropout at this rate (secondary line, no oracle leg)")
-    ap.add_argument("--copy-mib", type=int, default=0,
-                    help="only run a plain device-to-device copy of this many MiB, --steps "
-                         "times (the known-size kernel that scales the HBM byte counters)")
-    args = ap.parse_args()
-    if args.summarize_counters:
-        fc, wc, cfc, cwc, mib = args.summarize_counters
-        print(json.dumps(summarize_counters(fc, wc, cfc, cwc, int(mib) << 20, TRAFFIC_FILE)))
-        return
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs the per-head kernels on a single "
-              "MI355X; --gpus above 1 is not supported", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    import io_aware_tiled_05_amd as fa
-    from workloads import WORKLOADS, make_inputs
-
-    if args.copy_mib:
-        n = args.copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "steps": args.steps}))
-        return
-
-    if args.decode:
-        bench_decode(args, fa, torch, np)
-        return
-
-    w = WORKLOADS[args.workload]
-    if w.block_sparse or w.key_padding or w.dtype not in ("bf16", "f16"):
-        raise SystemExit("bench.py times the dense (optionally causal) 16-bit path")
+def bench_workload(args, w, fa, torch, np, with_cpu):
+    """One JSON record: K timed steps (forward + the three backward launches,
+    or the dropout pair) of workload ``w``."""
+    if w.dtype not in ("bf16", "f16"):
+        raise SystemExit("bench.py times the 16-bit path")
+    if args.dropout > 0 and (w.key_padding or w.block_sparse):
+        raise SystemExit("--dropout is timed on dense (optionally causal) workloads")
+    from workloads import make_inputs
     fa.load()
     dev = torch.device("cuda:0")
     x = make_inputs(w)
@@ -271,6 +248,8 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d) // 4, dtype=torch.float32, device=dev)
     scale, causal = x["scale"], w.causal
+    kl = None if x["key_len"] is None else torch.from_numpy(x["key_len"]).to(dev)
+    bm = None if x["block_mask"] is None else torch.from_numpy(x["block_mask"]).to(dev)
     stream = torch.cuda.current_stream()
     drop_p, drop_seed = float(args.dropout), 0x5EED_0001_2345_6789
     if not 0.0 <= drop_p < 1.0:
@@ -289,11 +268,15 @@ def main():
             if ev is not None:
                 ev[2].record(stream)
             return
-        fa.fa_fwd(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
+        if bm is not None:
+            fa.fa_fwd_blocksparse(q, k, v, bm, scale=scale, out=o, lse=lse)
+        else:
+            fa.fa_fwd(q, k, v, scale=scale, causal=causal, key_len=kl, out=o, lse=lse)
         if ev is not None:
             ev[1].record(stream)
         for i, st in enumerate((fa.FA_BWD_STAGE_D, fa.FA_BWD_STAGE_DKDV, fa.FA_BWD_STAGE_DQ)):
-            fa.fa_bwd_stage(st, q, k, v, o, lse, dO, dq, dk, dv, ws, scale=scale, causal=causal)
+            fa.fa_bwd_stage(st, q, k, v, o, lse, dO, dq, dk, dv, ws, scale=scale, causal=causal,
+                            key_len=kl, block_mask=bm)
             if ev is not None:
                 ev[2 + i].record(stream)
 
@@ -316,7 +299,7 @@ def main():
     kms = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
            for j, nm in enumerate(names)}
 
-    P = pairs_of(w)
+    P = visible_pairs(w, x)
     fwd_flops, bwd_flops = 4 * d * P, 10 * d * P
     total_tflops = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
     bwd_ms = kms["bwd"] if drop_p > 0.0 else kms["bwd_pre"] + kms["bwd_dkdv"] + kms["bwd_dq"]
@@ -333,13 +316,21 @@ def main():
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None if drop_p > 0.0 else measured_traffic(dom)}
+                # the committed counters were taken on the long causal workload
+                "traffic": measured_traffic(dom) if drop_p == 0.0 and w.name == "long_causal"
+                else None}
 
     metric = "attention fwd+bwd TFLOPS & % MFMA peak, bf16 d=64, N=1K-16K, 1 GPU"
     if d != 64:
         metric = metric.replace("d=64", f"d={d}")
+    if w.dtype != "bf16":
+        metric = metric.replace("bf16", "fp16")
     config = {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": causal,
-              "scale": scale, "parallelism": "none (1 GPU)"}
+              "scale": scale, "parallelism": "none (1 GPU)", "visible_pairs": P}
+    if kl is not None:
+        config["key_len"] = [int(v) for v in x["key_len"]]
+    if bm is not None:
+        config["block_density"] = round(float(x["block_mask"].mean()), 4)
     if drop_p > 0.0:
         metric = f"attention fwd+bwd with dropout p={drop_p:g} TFLOPS, bf16 d={d}, 1 GPU"
         config["dropout_p"] = drop_p
@@ -365,9 +356,69 @@ def main():
         "kernel_ms": {nm: round(v, 4) for nm, v in kms.items()},
         "wall_s_timed": round(t_wall, 3),
         "roofline": roofline,
-        "cpu_baseline": None if args.no_cpu_baseline or drop_p > 0.0 else cpu_baseline(x, w),
+        "cpu_baseline": cpu_baseline(x, w) if with_cpu else None,
     }
-    print(json.dumps(out), flush=True)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_causal")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV",
+                    "COPY_FETCH_CSV", "COPY_WRITE_CSV", "COPY_MIB"),
+                    help="write profiles/hbm_traffic.json from rocprofv3 --pmc csv files and exit")
+    ap.add_argument("--decode", action="store_true",
+                    help="time fa_decode on the long-context decode shape instead")
+    ap.add_argument("--sweep", action="store_true",
+                    help="one line per point of the sequence-length sweep (H=16, B=16384/N, "
+                         "N=1K..16K, d=64, bf16, causal and not) instead")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="time the step with dropout at this rate (secondary line, no oracle leg)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, --steps "
+                         "times (the known-size kernel that scales the HBM byte counters)")
+    args = ap.parse_args()
+    if args.summarize_counters:
+        fc, wc, cfc, cwc, mib = args.summarize_counters
+        print(json.dumps(summarize_counters(fc, wc, cfc, cwc, int(mib) << 20, TRAFFIC_FILE)))
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs the per-head kernels on a single "
+              "MI355X; --gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import io_aware_tiled_05_amd as fa
+    from workloads import SWEEP, WORKLOADS
+
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "steps": args.steps}))
+        return
+
+    if args.decode:
+        bench_decode(args, fa, torch, np)
+        return
+
+    if args.sweep:
+        for w in SWEEP:
+            out = bench_workload(args, w, fa, torch, np, with_cpu=False)
+            print(json.dumps(out), flush=True)
+        return
+    w = WORKLOADS[args.workload]
+    with_cpu = not (args.no_cpu_baseline or w.key_padding or w.block_sparse or args.dropout > 0)
+    print(json.dumps(bench_workload(args, w, fa, torch, np, with_cpu)), flush=True)
 
 
 if __name__ == "__main__":

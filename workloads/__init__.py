@@ -17,6 +17,8 @@ N(0, 1) because the datasets and trained models are not available):
 * ``block_sparse`` B=1  H=8  N=65536 d=64  bf16, 128x128 block mask: a band of
   3 blocks either side of the diagonal plus seeded random off-band blocks to
   about 5 % density (Path-256 length 64K)
+* ``sweep_{causal,full}_{1,2,4,8,16}k``  H=16, N=1K..16K, B=16384/N, d=64,
+  bf16 (the metric's sequence-length range at a fixed token count)
 
 Random streams: ``numpy.random.Generator(PCG64(SeedSequence(seed)))`` spawned
 into independent child streams for q, k, v, dO, lengths/mask and samples.
@@ -72,6 +74,16 @@ WORKLOADS = {
                              seed=5, sample_rows=256, sample_keys=64, sample_key_heads=1,
                              sample_key_blocks=8),
 }
+
+# Sequence-length sweep: the same 16384 tokens per head at every length
+# (B = 16384 / N), H = 16, d = 64, bf16, causal and non-causal; seed
+# 100 + log2 N.
+SWEEP_N = (1024, 2048, 4096, 8192, 16384)
+SWEEP = tuple(
+    Workload(f"sweep_{'causal' if c else 'full'}_{n // 1024}k", 16384 // n, 16, n, 64, "bf16",
+             causal=c, seed=100 + int(math.log2(n)), sample_rows=256, sample_keys=64)
+    for c in (True, False) for n in SWEEP_N)
+WORKLOADS.update({w.name: w for w in SWEEP})
 
 
 def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
