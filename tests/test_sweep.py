@@ -12,7 +12,7 @@ import pytest
 
 from helpers import TOL, assert_close, to_dev, to_np
 from oracle import attention_key_grads, attention_rows
-from workloads import SWEEP, make_inputs, sample_key_rows, sample_rows
+from workloads import SWEEP, Workload, make_inputs, sample_key_rows, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +24,14 @@ def fa():
     return fa
 
 
-@pytest.mark.parametrize("w", SWEEP, ids=[w.name for w in SWEEP])
+# ragged length with a grid of more than two 4-wave workgroups per compute
+# unit (the small test shapes run the 2-wave forward)
+RAGGED = tuple(Workload(f"ragged_{'causal' if c else 'full'}_1000", 16, 16, 1000, 64, "bf16",
+                        causal=c, seed=120 + c, sample_rows=256, sample_keys=64)
+               for c in (True, False))
+
+
+@pytest.mark.parametrize("w", SWEEP + RAGGED, ids=[w.name for w in SWEEP + RAGGED])
 def test_sweep_sampled_rows(fa, w):
     import torch
     x = make_inputs(w)
