@@ -146,11 +146,11 @@ __device__ __forceinline__ uint32_t absmax8(u32x4 a) {
 // Per row: D_i = sum_c dO_ic O_ic and shift_i = lse_i * log2(e) (+inf when
 // the row saw no key, so that exp2(c s - shift) = 0 there).  STATS (bf16
 // inputs): also max |Q|, |K|, |V|, |dO| per (b, h), into maxes[4][BH]
-// (zeroed before).  Grid (B*H, chunks of rows): a workgroup stays
-// inside one (b, h), reduces its maxima and issues one atomic max per
-// tensor, so each address sees N / kPreRows atomics.
+// (zeroed before).  Grid (B*H, chunks of `iters` row groups): a workgroup
+// stays inside one (b, h), reduces its maxima and issues one atomic max per
+// tensor, so each address sees one atomic per chunk.
 // ---------------------------------------------------------------------------
-constexpr int kPreIter = 16;  // row groups per workgroup in the D pass
+constexpr int kPreIter = 16;  // most row groups per workgroup in the D pass
 
 // threads per row in the D pass: one per 8 elements (16 bytes), rounded up
 // to a power of two for the shuffle reduction (d = 96: 16, the last 4 idle)
@@ -164,16 +164,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
                                                       const float* lse, const uint16_t* q,
                                                       const uint16_t* k, const uint16_t* v,
                                                       float* Dbuf, float* shift,
-                                                      uint32_t* maxes, int N, int BH) {
+                                                      uint32_t* maxes, int N, int BH,
+                                                      int iters) {
   constexpr int TPR = pre_tpr<D>();  // threads per row, 8 elements (16 B) each
   constexpr int RPB = 256 / TPR;      // rows per pass of the workgroup
   const int bh = blockIdx.x;
   const int c = (int)(threadIdx.x % TPR) * 8;
   const bool col_ok = c < D;
   uint32_t mx[4] = {0u, 0u, 0u, 0u};
-  const int r_begin = blockIdx.y * RPB * kPreIter;
+  const int r_begin = blockIdx.y * RPB * iters;
 #pragma unroll 4
-  for (int it = 0; it < kPreIter; ++it) {
+  for (int it = 0; it < iters; ++it) {
     const int r = r_begin + it * RPB + (int)(threadIdx.x / TPR);  // row inside this (b, h)
     const bool ok = r < N;
     const int64_t row = (int64_t)bh * N + r;
@@ -820,7 +821,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
 #define FA_BWD_INSTANTIATE(T, D)                                                  \
   template __global__ void bwd_pre_kernel<T, D, true>(                            \
       const uint16_t*, const uint16_t*, const float*, const uint16_t*, const uint16_t*, \
-      const uint16_t*, float*, float*, uint32_t*, int, int);                        \
+      const uint16_t*, float*, float*, uint32_t*, int, int, int);                   \
   template __global__ void bwd_dkdv_kernel<T, D, true, false, false>(BwdParams);   \
   template __global__ void bwd_dkdv_kernel<T, D, false, false, false>(BwdParams);  \
   template __global__ void bwd_dkdv_kernel<T, D, false, true, false>(BwdParams);   \
@@ -869,11 +870,21 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
                        maxes, 4 * BH);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    constexpr int pre_rows = 256 / pre_tpr<D>() * kPreIter;  // rows per workgroup
+    // row groups per workgroup: up to kPreIter, fewer when that would leave
+    // the grid below about 2048 workgroups (short sequences, few heads), but
+    // never more than 32 workgroups per head (each issues an atomic max on
+    // the head's 4 maxima; more contend: 128 per head took 103 instead of
+    // 72 us at N = 16384, H = 16)
+    constexpr int rpb = 256 / pre_tpr<D>();  // rows per group
+    const int64_t groups = (a.N + rpb - 1) / rpb;
+    const int64_t by_head = (groups + 31) / 32, by_grid = (groups * BH + 2047) / 2048;
+    int iters = (int)(by_head > by_grid ? by_head : by_grid);
+    iters = iters < 1 ? 1 : (iters > kPreIter ? kPreIter : iters);
+    const int pre_rows = rpb * iters;  // rows per workgroup
     hipLaunchKernelGGL((bwd_pre_kernel<T, D, true>), dim3(BH, (a.N + pre_rows - 1) / pre_rows),
                        dim3(256), 0, a.stream, static_cast<const uint16_t*>(a.o), dO, a.lse, q,
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), Dbuf,
-                       shift, maxes, a.N, BH);
+                       shift, maxes, a.N, BH, iters);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_convert_kernel<T, D>), dim3(row_blocks), dim3(256), 0, a.stream, q,
