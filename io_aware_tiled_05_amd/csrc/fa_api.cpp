@@ -5,6 +5,7 @@
 // on the caller's stream.
 #include "fa.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -99,13 +100,18 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
 namespace fa {
 
 int device_cu_count() {
-  static int cached[64];  // per device id; 0 = not queried yet (benign race: same value)
+  // per device id; 0 = not queried yet.  Concurrent callers may both query
+  // and store the same value; the atomics make that well defined.
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-  if (dev < 64 && n > 0) cached[dev] = n;
+  if (dev < 64 && n > 0) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
