@@ -50,11 +50,19 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream):
+def _stream(stream, q):
     torch = _torch()
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(q.device)
     return stream.cuda_stream
+
+
+def _call(q, name, *args):
+    """The C entry point `name` with q's device current (the library launches
+    on the current device, which must be the one that owns the stream)."""
+    torch = _torch()
+    with torch.cuda.device(q.device):
+        return getattr(load(), name)(*args)
 
 
 def _key_len(key_len, q):
@@ -80,9 +88,8 @@ def fa_fwd(q, k, v, scale=None, causal=False, key_len=None, out=None, lse=None,
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_qkv(q, o)
-    st = load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
-                       _scale(scale, d), int(bool(causal)), _ptr(kl), _dtype_code(q),
-                       _stream(stream))
+    st = _call(q, "fa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+               _scale(scale, d), int(bool(causal)), _ptr(kl), _dtype_code(q), _stream(stream, q))
     check("fa_fwd", st)
     return o, lse
 
@@ -111,10 +118,9 @@ def fa_bwd(q, k, v, o, lse, dO, scale=None, causal=False, key_len=None, dq=None,
     kl = _key_len(key_len, q)
     dq, dk, dv, ws = _bwd_outputs(q, dq, dk, dv, workspace)
     _check_qkv(q, dq, dk, dv)
-    st = load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
-                       _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)),
-                       _ptr(kl), _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(q),
-                       _stream(stream))
+    st = _call(q, "fa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+               _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(kl),
+               _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(q), _stream(stream, q))
     check("fa_bwd", st)
     return dq, dk, dv
 
@@ -138,9 +144,8 @@ def fa_fwd_blocksparse(q, k, v, block_mask, block_size=128, scale=None, out=None
         raise ValueError(f"block_mask must be [{nb}, {nb}]")
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    st = load().fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
-                                   _scale(scale, d), _ptr(bm), block_size, _dtype_code(q),
-                                   _stream(stream))
+    st = _call(q, "fa_fwd_blocksparse", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+               _scale(scale, d), _ptr(bm), block_size, _dtype_code(q), _stream(stream, q))
     check("fa_fwd_blocksparse", st)
     return o, lse
 
@@ -155,11 +160,9 @@ def fa_bwd_blocksparse(q, k, v, o, lse, dO, block_mask, block_size=128, scale=No
     if bm.shape != (nb, nb):
         raise ValueError(f"block_mask must be [{nb}, {nb}]")
     dq, dk, dv, ws = _bwd_outputs(q, dq, dk, dv, workspace)
-    st = load().fa_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
-                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d),
-                                   _ptr(bm), block_size, _ptr(ws),
-                                   ws.numel() * ws.element_size(), _dtype_code(q),
-                                   _stream(stream))
+    st = _call(q, "fa_bwd_blocksparse", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d), _ptr(bm), block_size,
+               _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(q), _stream(stream, q))
     check("fa_bwd_blocksparse", st)
     return dq, dk, dv
 
@@ -172,12 +175,10 @@ def fa_bwd_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, workspace, scale=None, 
     B, H, N, d = q.shape
     kl = _key_len(key_len, q)
     bm = None if block_mask is None else _block_mask(block_mask, q)
-    st = load().fa_bwd_stage(int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                             _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
-                             _scale(scale, d), int(bool(causal)), _ptr(kl), _ptr(bm),
-                             block_size, _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _dtype_code(q),
-                             _stream(stream))
+    st = _call(q, "fa_bwd_stage", int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+               _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d),
+               int(bool(causal)), _ptr(kl), _ptr(bm), block_size, _ptr(workspace),
+               workspace.numel() * workspace.element_size(), _dtype_code(q), _stream(stream, q))
     check("fa_bwd_stage", st)
 
 
@@ -206,10 +207,9 @@ def fa_decode(q, k, v, scale=None, key_len=None, out=None, lse=None, workspace=N
     need = fa_decode_workspace_size(B, H, Nq, Nk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
-    st = load().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
-                          _scale(scale, d), _ptr(kl), _ptr(workspace),
-                          workspace.numel() * workspace.element_size(), _dtype_code(q),
-                          _stream(stream))
+    st = _call(q, "fa_decode", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+               _scale(scale, d), _ptr(kl), _ptr(workspace),
+               workspace.numel() * workspace.element_size(), _dtype_code(q), _stream(stream, q))
     check("fa_decode", st)
     return o, lse
 
@@ -233,9 +233,9 @@ def fa_fwd_dropout(q, k, v, dropout_p, seed, offset=0, scale=None, causal=False,
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_qkv(q, o)
-    st = load().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
-                               _scale(scale, d), int(bool(causal)), _ptr(kl), float(dropout_p),
-                               sd, off, _dtype_code(q), _stream(stream))
+    st = _call(q, "fa_fwd_dropout", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+               _scale(scale, d), int(bool(causal)), _ptr(kl), float(dropout_p), sd, off,
+               _dtype_code(q), _stream(stream, q))
     check("fa_fwd_dropout", st)
     return o, lse
 
@@ -250,10 +250,9 @@ def fa_bwd_dropout(q, k, v, o, lse, dO, dropout_p, seed, offset=0, scale=None, c
     sd, off = _seed(seed, offset)
     dq, dk, dv, ws = _bwd_outputs(q, dq, dk, dv, workspace)
     _check_qkv(q, dq, dk, dv)
-    st = load().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
-                               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d),
-                               int(bool(causal)), _ptr(kl), float(dropout_p), sd, off,
-                               _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(q),
-                               _stream(stream))
+    st = _call(q, "fa_bwd_dropout", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)),
+               _ptr(kl), float(dropout_p), sd, off, _ptr(ws), ws.numel() * ws.element_size(),
+               _dtype_code(q), _stream(stream, q))
     check("fa_bwd_dropout", st)
     return dq, dk, dv

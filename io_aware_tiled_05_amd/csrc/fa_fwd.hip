@@ -11,7 +11,9 @@
 // are written once, and no score ever leaves the chip.
 //
 // Work split (16-bit path): 256 threads = 4 waves per workgroup.  A wave
-// owns QW query rows (64 at d = 64, 32 at d = 128) held in registers as the
+// owns QW query rows (64 at d <= 64; 32 at d >= 96, with dropout, and for
+// block-sparse masks, whose workgroup covers one 128-query mask row) held
+// in registers as the
 // B operand of the transposed score tile S^T = K Q^T, computed with
 // v_mfma_f32_32x32x16: a lane holds 16 keys of one query column, so the
 // per-query reductions are in-lane plus one exchange with lane ^ 32, and
