@@ -43,7 +43,9 @@
  *   key_len[b] outside [0, N] is clamped to that range.  Rows that see no
  *   key get O = 0, lse = -inf and contribute nothing to the gradients.
  * Thread safety.  Every call is stateless; concurrent calls on different
- *   outputs are safe.
+ *   outputs (and, for the backward and decode, different workspaces) are
+ *   safe.  Kernels launch on the calling thread's current HIP device, which
+ *   must own `stream` and the tensors.
  */
 #ifndef FA_H
 #define FA_H
