@@ -46,7 +46,10 @@
 // geometric mean of max |c Q| and max |K| lies in [2^-4, 2^13]: then the
 // score accumulator, started at -shift, is exactly the exponent of P, and
 // the dP accumulator, started at -D, is exactly dP - D, so P costs one
-// exponential and dS one multiply.
+// exponential and dS one multiply.  Heads whose maxima allow large logits
+// (c max|Q| max|K| sqrt(d) > 64) leave c out of the Q copy, which rounding
+// c Q to fp16 would make inexact by ~2^-11 |c q.k| in the exponent, and
+// multiply the score accumulator by c 2^f in fp32 instead (see Scales).
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -94,15 +97,30 @@ constexpr int kTq = 13, kTk = 13, kTo = 3, kTv = 2;  // targets: max' in [2^t, 2
 __device__ __forceinline__ int exp_of(uint32_t bits) { return (int)((bits >> 23) & 0xffu) - 127; }
 __device__ __forceinline__ int clamp60(int e) { return e < -60 ? -60 : (e > 60 ? 60 : e); }
 
-// Per-(b, h) exponents of the fp16 operands of the dK/dV products:
-// Q'' = c Q 2^-eq, K' = K 2^-ek, V' = V 2^-ev, dO' = dO 2^-eo, c S = 2^f S''.
+// Per-(b, h) exponents of the fp16 operands of the products:
+// Q'' = c Q 2^-eq (exact: Q 2^-eq), K' = K 2^-ek, V' = V 2^-ev,
+// dO' = dO 2^-eo, and c S = m S'' with m = 2^f (exact: c 2^f), f = eq + ek.
+// Folding c into the fp16 copy of Q rounds c Q to 11 bits, which moves a
+// score by about 2^-11 |c q.k| / sqrt(d) in base-2 units: nothing for
+// ordinary logits, but percent-level errors in P once |c q.k| reaches the
+// hundreds.  A head whose maxima allow that (c max|Q| max|K| sqrt(d) > 64)
+// is "exact": its Q copy is only scaled by a power of two (exact), and the
+// score accumulator is multiplied by m in fp32 (one multiply per score).
 struct Scales {
   int eq, ek, ev, eo, f;
+  bool exact;  // c not folded into the Q copy
+  bool mul;    // the score accumulator needs the factor m (m != 1)
+  float m;     // c S = m S''
 };
 
+template <int D>
 __device__ __forceinline__ Scales bwd_scales(const uint32_t* maxes, int BH, int bh, float c) {
   Scales s;
-  const uint32_t mq = __builtin_bit_cast(uint32_t, c * __builtin_bit_cast(float, maxes[bh]));
+  const float qmax = __builtin_bit_cast(float, maxes[bh]);
+  const float kmax = __builtin_bit_cast(float, maxes[BH + bh]);
+  const float bound = c * qmax * kmax;
+  s.exact = bound * bound * (float)D > 4096.f;
+  const uint32_t mq = __builtin_bit_cast(uint32_t, s.exact ? qmax : c * qmax);
   const uint32_t mk = maxes[BH + bh];
   s.ev = scale_exp(maxes[2 * BH + bh], kTv);
   s.eo = scale_exp(maxes[3 * BH + bh], kTo);
@@ -120,6 +138,8 @@ __device__ __forceinline__ Scales bwd_scales(const uint32_t* maxes, int BH, int 
     }
   }
   s.f = s.eq + s.ek;
+  s.m = s.exact ? ldexpf(c, s.f) : ldexpf(1.f, s.f);
+  s.mul = s.exact || s.f != 0;
   return s;
 }
 
@@ -245,8 +265,8 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, con
   const int64_t row = gid / TPR;
   const int col = (int)(gid % TPR) * 8;
   if (row >= rows) return;
-  const Scales sc = bwd_scales(maxes, BH, (int)(row / N), c);
-  const float cq = ldexpf(c, -sc.eq);
+  const Scales sc = bwd_scales<D>(maxes, BH, (int)(row / N), c);
+  const float cq = ldexpf(sc.exact ? 1.f : c, -sc.eq);
   const u32x4 a = *reinterpret_cast<const u32x4*>(q + row * D + col);
   const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + col);
   const u32x4 kk = *reinterpret_cast<const u32x4*>(k + row * D + col);
@@ -264,7 +284,7 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, con
   *reinterpret_cast<u32x4*>(k16 + row * D + col) = rk;
   if (col == 0) {
     nDs[row] = -ldexpf(Dbuf[row], -(sc.eo + sc.ev));
-    nsh[row] = -ldexpf(shift[row], -sc.f);
+    nsh[row] = sc.exact ? -shift[row] / sc.m : -ldexpf(shift[row], -sc.f);
   }
 }
 
@@ -366,7 +386,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
   const float* nD = p.nDs + (size_t)bh * N;
   const int L = valid_keys(p.key_len, b, N);
   const int k0 = kt * kBKV, kw = k0 + wave * 32, key = kw + l32;
-  const Scales sc = bwd_scales(p.maxes, p.BH, bh, p.c);
+  const Scales sc = bwd_scales<D>(p.maxes, p.BH, bh, p.c);
   const int ek = sc.ek, ev = sc.ev;
 
   // this wave's keys and values as B operands (lane = key, k = d values)
@@ -436,8 +456,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
       }
     // P = exp2(c s - shift_row), dS' = P (dP - D_row) 2^-(eo+ev)
     const bool need_mask = (kw + 32 > L) || (q0 + kBQ > N) || (CAUSAL && q0 < kw + 31);
-    if (sc.f != 0) {  // unbalanced operand scales (extreme input ranges only)
-      const float sf = ldexpf(1.f, sc.f);
+    if (sc.mul) {  // exact head or unbalanced operand scales (large or extreme ranges)
+      const float sf = sc.m;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) s[qb] *= sf;
     }
@@ -571,10 +591,11 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
     }
   }
 
-  // store dK = scale/c 2^(eq+eo+ev) dK'^T^T (scale/c = ln 2) and dV = 2^eo dV'
-  // (4 consecutive d per store)
+  // store dK = scale/c 2^(eq+eo+ev) dK'^T^T (scale/c = ln 2; an exact head's
+  // Q copy carries no c: scale) and dV = 2^eo dV' (4 consecutive d per store)
   if (key < N) {
     const int ekk = sc.eq + sc.eo + sc.ev;
+    const float kmul = sc.exact ? p.scale : kLn2;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -583,7 +604,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
         f32x4 k4, v4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          k4[j] = ldexpf(dk[db][4 * i + j] * kLn2, ekk);
+          k4[j] = ldexpf(dk[db][4 * i + j] * kmul, ekk);
           v4[j] = ldexpf(dv[db][4 * i + j], sc.eo);
         }
         *reinterpret_cast<u32x2*>(p.dk + off) = pack4<T>(k4);
@@ -627,7 +648,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
   const uint16_t* V = p.v + base;
   const int L = valid_keys(p.key_len, b, N);
   const int q0 = qt * kBR, qw = q0 + wave * 32, query = qw + l32;
-  const Scales sc = bwd_scales(p.maxes, p.BH, bh, p.c);
+  const Scales sc = bwd_scales<D>(p.maxes, p.BH, bh, p.c);
   // D of this lane's query (dropout: subtracted after the mask)
   const float dq_D = DROP && query < N ? p.Dbuf[(size_t)bh * N + query] : 0.f;
 
@@ -696,8 +717,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
       }
     prefetch();
     const bool need_mask = (kt0 + kBC > L) || (CAUSAL && kt0 + kBC - 1 > qw);
-    if (sc.f != 0) {  // unbalanced operand scales (extreme input ranges only)
-      const float sf = ldexpf(1.f, sc.f);
+    if (sc.mul) {  // exact head or unbalanced operand scales (large or extreme ranges)
+      const float sf = sc.m;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] *= sf;
     }
