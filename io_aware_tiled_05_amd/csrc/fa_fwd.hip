@@ -56,9 +56,6 @@ struct FwdParams {
 };
 
 // Compile-time tuning knobs (defaults are the measured best).
-#ifndef FA_FWD_QW64
-#define FA_FWD_QW64 64  // queries per wave at d = 64 (32 or 64)
-#endif
 #ifndef FA_FWD_WAVES_PER_SIMD
 #define FA_FWD_WAVES_PER_SIMD 2
 #endif
@@ -76,24 +73,22 @@ __device__ __forceinline__ int valid_keys(const int32_t* key_len, int b, int N) 
 
 template <int D>
 struct FwdShape {
-  static constexpr int QW = D <= 64 ? FA_FWD_QW64 : 32;  // queries per wave
+  static constexpr int QW = D <= 64 ? 64 : 32;  // default queries per wave
   static constexpr int NQB = QW / 32;           // 32-query MFMA blocks per wave
   static constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;             // 32-row blocks of O^T
   static constexpr int TILE = kBC * D;          // elements per K or V tile
 };
 
-// NW waves per workgroup; a workgroup covers NW * QW queries.
+// NW waves per workgroup of QW (32 or 64) queries each; a workgroup covers
+// NW * QW queries.
 // DROP: dropout on P before the product with V (P kept with probability
 // 1 - p and scaled by 1 / (1 - p); the row sum l and lse use P itself).
-template <typename T, int D, int NW, bool CAUSAL, bool SPARSE, bool DROP>
+template <typename T, int D, int NW, int QW, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(FwdParams p) {
   typedef FwdShape<D> Sh;
-  // with dropout a wave takes 32 queries (the generator's registers do not
-  // fit next to two query blocks); block-sparse too, so that four waves
-  // share each K/V tile of a 128-query mask row (measured 3-5 % faster than
-  // two waves of 64 queries)
-  constexpr int QW = (DROP || SPARSE) ? 32 : Sh::QW, NQB = QW / 32, KS = Sh::KS, DB = Sh::DB;
+  static_assert(QW == 32 || QW == 64, "a wave holds one or two 32-query blocks");
+  constexpr int NQB = QW / 32, KS = Sh::KS, DB = Sh::DB;
   constexpr int TILE = Sh::TILE;
   constexpr int BR = NW * QW;
   typedef typename Elt<T>::vec8 vec8;
@@ -512,12 +507,17 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParamsF32 p) {
 // (Without them the host pass of this compiler leaves some kernel-template
 // launch stubs undefined.)
 #define FA_FWD_INSTANTIATE(T, D)                                                              \
-  template __global__ void fwd_kernel<T, D, 4, false, true, false>(                          \
+  template __global__ void fwd_kernel<T, D, 4, 32, false, true, false>(FwdParams);           \
+  template __global__ void fwd_kernel<T, D, 4, FwdShape<D>::QW, true, false, false>(          \
       FwdParams);                                                                            \
-  template __global__ void fwd_kernel<T, D, 4, true, false, false>(FwdParams);               \
-  template __global__ void fwd_kernel<T, D, 4, false, false, false>(FwdParams);              \
-  template __global__ void fwd_kernel<T, D, 4, true, false, true>(FwdParams);                \
-  template __global__ void fwd_kernel<T, D, 4, false, false, true>(FwdParams);
+  template __global__ void fwd_kernel<T, D, 4, FwdShape<D>::QW, false, false, false>(         \
+      FwdParams);                                                                            \
+  template __global__ void fwd_kernel<T, D, 4, 32, true, false, true>(FwdParams);            \
+  template __global__ void fwd_kernel<T, D, 4, 32, false, false, true>(FwdParams);
+// the 32-query dense kernels that small grids select where 64 is the default
+#define FA_FWD_INSTANTIATE_SMALL(T, D)                                                        \
+  template __global__ void fwd_kernel<T, D, 4, 32, true, false, false>(FwdParams);           \
+  template __global__ void fwd_kernel<T, D, 4, 32, false, false, false>(FwdParams);
 
 #define FA_FWD_INSTANTIATE_D(D)                                                               \
   FA_FWD_INSTANTIATE(__bf16, D)                                                              \
@@ -528,13 +528,18 @@ FA_FWD_INSTANTIATE_D(32)
 FA_FWD_INSTANTIATE_D(64)
 FA_FWD_INSTANTIATE_D(96)
 FA_FWD_INSTANTIATE_D(128)
+static_assert(FwdShape<32>::QW == 64 && FwdShape<64>::QW == 64, "small-grid variants below");
+FA_FWD_INSTANTIATE_SMALL(__bf16, 32)
+FA_FWD_INSTANTIATE_SMALL(_Float16, 32)
+FA_FWD_INSTANTIATE_SMALL(__bf16, 64)
+FA_FWD_INSTANTIATE_SMALL(_Float16, 64)
+#undef FA_FWD_INSTANTIATE_SMALL
 #undef FA_FWD_INSTANTIATE_D
 #undef FA_FWD_INSTANTIATE
 
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
-hipError_t run_fwd(const FwdArgs& a) {
+template <typename T, int D, int QW, bool CAUSAL, bool SPARSE, bool DROP>
+hipError_t launch_fwd_kernel(const FwdArgs& a) {
   // block-sparse workgroups cover exactly one 128-query mask row
-  constexpr int QW = (DROP || SPARSE) ? 32 : FwdShape<D>::QW;
   constexpr int NW = SPARSE ? 128 / QW : 4;
   constexpr int BR = NW * QW;
   FwdParams p;
@@ -554,10 +559,29 @@ hipError_t run_fwd(const FwdArgs& a) {
   p.nblk = (a.N + 127) / 128;
   p.drop = a.drop;
   const int wgs_per_head = CAUSAL && !SPARSE ? (p.nqt + 1) / 2 : p.nqt;
-  hipLaunchKernelGGL((fwd_kernel<T, D, NW, CAUSAL, SPARSE, DROP>), dim3(wgs_per_head * p.BH),
-                     dim3(64 * NW),
-                     0, a.stream, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, NW, QW, CAUSAL, SPARSE, DROP>),
+                     dim3(wgs_per_head * p.BH), dim3(64 * NW), 0, a.stream, p);
   return hipGetLastError();
+}
+
+// Queries per wave: 32 with dropout (the generator's registers do not fit
+// next to two query blocks) and for block-sparse masks (four waves share
+// each K/V tile of a 128-query mask row: measured 3-5 % faster than two
+// waves of 64 queries).  Dense 64-query waves at d <= 64 halve the LDS
+// reads per MFMA, but when their grid has fewer workgroups than the GPU has
+// compute units, 32-query waves (twice the workgroups) finish sooner
+// (causal B = 8, H = 12, N = 1024: 192 -> 384 workgroups, 45.6 -> 37.0 us;
+// with 256 workgroups on 256 CUs, 64-query waves stay ahead).
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+hipError_t run_fwd(const FwdArgs& a) {
+  constexpr int QW = (DROP || SPARSE) ? 32 : FwdShape<D>::QW;
+  if constexpr (QW == 64) {
+    const int nqt = (a.N + 4 * QW - 1) / (4 * QW);
+    const long wgs = (long)(CAUSAL ? (nqt + 1) / 2 : nqt) * a.B * a.H;
+    const int cus = device_cu_count();
+    if (cus > 0 && wgs < cus) return launch_fwd_kernel<T, D, 32, CAUSAL, SPARSE, DROP>(a);
+  }
+  return launch_fwd_kernel<T, D, QW, CAUSAL, SPARSE, DROP>(a);
 }
 
 template <int D, bool CAUSAL>
