@@ -85,12 +85,13 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const int32_t* key_len, int dtype, void* stream);
 
 /* Bytes of device workspace fa_bwd / fa_bwd_blocksparse need, about
- * 16*B*H*N + 6*B*H*N*d + 16*B*H (each region rounded up to 256 bytes):
+ * 16*B*H*N + 6*B*H*N*d + 2064*B*H (each region rounded up to 256 bytes):
  * per query row, D_i = sum_c dO_ic O_ic, the base-2 softmax shift
  * lse_i * log2(e) (+inf for rows without keys) and their power-of-two
  * scaled negations (four floats), and 16-bit copies of the row's q, k and
  * dO scaled by powers of two; per (b, h), the maxima of |q|, |k|, |v|,
- * |dO| that choose those powers.  Linear in N: the method's memory grows
+ * |dO| that choose those powers and the partial maxima of at most 128
+ * workgroups of the D pass that they are reduced from.  Linear in N: the method's memory grows
  * linearly, not quadratically, in sequence length ([ODP "Why it
  * mattered"]).  Returns 0 for invalid sizes. */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
@@ -99,8 +100,7 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * Picture: Why Tiling Wins"]): the probabilities are rebuilt on-chip from
  * q, k and lse; nothing of size N x N is stored.  Launches on `stream`:
  * D = rowsum(dO * O) with the operand copies; dK/dV (one workgroup per key tile);
- * dQ (one workgroup per query tile).  Deterministic: the only atomics take
- * maxima, whose result does not depend on order.
+ * dQ (one workgroup per query tile).  Deterministic: no atomics.
  *   o, lse  : the forward's outputs for the same inputs and mask
  *   dO      : upstream gradient [B][H][N][d], dtype
  *   dq,dk,dv: outputs [B][H][N][d], dtype (overwritten)

@@ -13,12 +13,13 @@
 // D_i = sum_c dO_ic O_ic (= sum_j P_ij dP_ij), dQ = scale dS K,
 // dK = scale dS^T Q.
 //
-// Stages (deterministic: the only atomics take per-head maxima):
+// Stages (deterministic: no atomics):
 //   bwd_pre   per query row: D and the base-2 softmax shift lse*log2(e)
-//             (+inf for rows without keys), into the workspace, and the
-//             per-(b, h) maxima of |Q|, |K|, |V|, |dO| (bwd_zero clears
-//             them first); bwd_convert then writes the scaled fp16 copies
-//             of Q, K, dO and the scaled row terms described below;
+//             (+inf for rows without keys), into the workspace, and each
+//             workgroup's maxima of |Q|, |K|, |V|, |dO|; bwd_convert
+//             reduces those to per-(b, h) maxima and writes the scaled
+//             fp16 copies of Q, K, dO and the scaled row terms described
+//             below;
 //   bwd_dkdv  one workgroup per 128 keys (32 per wave); query tiles of 64
 //             rows (Q, dO, row terms) are double buffered in LDS.  With
 //             v_mfma_f32_32x32x16, S = Q K^T and dP = dO V^T come out with
@@ -113,17 +114,19 @@ struct Scales {
   float m;     // c S = m S''
 };
 
+// mx: max |Q|, |K|, |V|, |dO| of the (b, h) as float bit patterns
 template <int D>
-__device__ __forceinline__ Scales bwd_scales(const uint32_t* maxes, int BH, int bh, float c) {
+__device__ __forceinline__ Scales bwd_scales_of(uint32_t mxq, uint32_t mxk, uint32_t mxv,
+                                                uint32_t mxo, float c) {
   Scales s;
-  const float qmax = __builtin_bit_cast(float, maxes[bh]);
-  const float kmax = __builtin_bit_cast(float, maxes[BH + bh]);
+  const float qmax = __builtin_bit_cast(float, mxq);
+  const float kmax = __builtin_bit_cast(float, mxk);
   const float bound = c * qmax * kmax;
   s.exact = bound * bound * (float)D > 4096.f;
   const uint32_t mq = __builtin_bit_cast(uint32_t, s.exact ? qmax : c * qmax);
-  const uint32_t mk = maxes[BH + bh];
-  s.ev = scale_exp(maxes[2 * BH + bh], kTv);
-  s.eo = scale_exp(maxes[3 * BH + bh], kTo);
+  const uint32_t mk = mxk;
+  s.ev = scale_exp(mxv, kTv);
+  s.eo = scale_exp(mxo, kTo);
   if (mq == 0u || mk == 0u) {
     s.eq = s.ek = 0;
   } else {
@@ -143,9 +146,10 @@ __device__ __forceinline__ Scales bwd_scales(const uint32_t* maxes, int BH, int 
   return s;
 }
 
-__global__ __launch_bounds__(256) void bwd_zero_kernel(uint32_t* p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0u;
+// the same from the maxima stored per (b, h) in maxes[4][BH]
+template <int D>
+__device__ __forceinline__ Scales bwd_scales(const uint32_t* maxes, int BH, int bh, float c) {
+  return bwd_scales_of<D>(maxes[bh], maxes[BH + bh], maxes[2 * BH + bh], maxes[3 * BH + bh], c);
 }
 
 // largest |x| of the 8 16-bit values in a 16-byte chunk, as float bits
@@ -164,13 +168,13 @@ __device__ __forceinline__ uint32_t absmax8(u32x4 a) {
 
 // ---------------------------------------------------------------------------
 // Per row: D_i = sum_c dO_ic O_ic and shift_i = lse_i * log2(e) (+inf when
-// the row saw no key, so that exp2(c s - shift) = 0 there).  STATS (bf16
-// inputs): also max |Q|, |K|, |V|, |dO| per (b, h), into maxes[4][BH]
-// (zeroed before).  Grid (B*H, chunks of `iters` row groups): a workgroup
-// stays inside one (b, h), reduces its maxima and issues one atomic max per
-// tensor, so each address sees one atomic per chunk.
+// the row saw no key, so that exp2(c s - shift) = 0 there).  STATS: also
+// max |Q|, |K|, |V|, |dO| of the workgroup's rows, stored as its partial
+// maxima part[4][BH][kPreChunks] (no atomics, so nothing has to be cleared
+// first: the convert pass reduces exactly the gridDim.y partials that this
+// launch wrote).  Grid (B*H, chunks of `iters` row groups): a workgroup
+// stays inside one (b, h).
 // ---------------------------------------------------------------------------
-constexpr int kPreIter = 16;  // most row groups per workgroup in the D pass
 
 // threads per row in the D pass: one per 8 elements (16 bytes), rounded up
 // to a power of two for the shuffle reduction (d = 96: 16, the last 4 idle)
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
                                                       const float* lse, const uint16_t* q,
                                                       const uint16_t* k, const uint16_t* v,
                                                       float* Dbuf, float* shift,
-                                                      uint32_t* maxes, int N, int BH,
+                                                      uint32_t* part, int N, int BH,
                                                       int iters) {
   constexpr int TPR = pre_tpr<D>();  // threads per row, 8 elements (16 B) each
   constexpr int RPB = 256 / TPR;      // rows per pass of the workgroup
@@ -244,47 +248,75 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
       uint32_t m = red[threadIdx.x][0];
 #pragma unroll
       for (int w = 1; w < 4; ++w) m = m > red[threadIdx.x][w] ? m : red[threadIdx.x][w];
-      atomicMax(maxes + (size_t)threadIdx.x * BH + bh, m);
+      part[((size_t)threadIdx.x * BH + bh) * kPreChunks + blockIdx.y] = m;
     }
   }
 }
 
 // c Q * 2^-eq, K * 2^-ek and dO * 2^-eo as fp16; -shift * 2^-f and -D * 2^-(eo+ev)
 // per row (the initial values of the dK/dV kernel's score and dP
-// accumulators).
+// accumulators).  Workgroup (b, h) = blockIdx.x / rbph, `iters` blocks of
+// RPB rows from row (blockIdx.x % rbph) * iters * RPB.  Every wave reduces
+// the head's nchunk partial maxima from the D pass itself (iters > 1 on
+// large grids spreads that over more rows); the head's first workgroup
+// also stores them in maxes[4][BH] for the dK/dV and dQ kernels.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, const uint16_t* k,
                                                           const uint16_t* dO, const float* Dbuf,
                                                           const float* shift,
-                                                          const uint32_t* maxes, float c,
+                                                          const uint32_t* part, int nchunk,
+                                                          uint32_t* maxes, float c,
                                                           uint16_t* q16, uint16_t* k16,
                                                           uint16_t* do16, float* nDs, float* nsh,
-                                                          int64_t rows, int N, int BH) {
-  constexpr int TPR = D / 8;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / TPR;
-  const int col = (int)(gid % TPR) * 8;
-  if (row >= rows) return;
-  const Scales sc = bwd_scales<D>(maxes, BH, (int)(row / N), c);
-  const float cq = ldexpf(sc.exact ? 1.f : c, -sc.eq);
-  const u32x4 a = *reinterpret_cast<const u32x4*>(q + row * D + col);
-  const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + col);
-  const u32x4 kk = *reinterpret_cast<const u32x4*>(k + row * D + col);
-  u32x4 ra, rg, rk;
+                                                          int N, int BH, int rbph, int iters) {
+  constexpr int TPR = D / 8;       // threads per row, 16 bytes each
+  constexpr int RPB = 256 / TPR;   // rows per workgroup (d = 96: 21, 4 threads idle)
+  const int bh = (int)(blockIdx.x / (unsigned)rbph), rb = (int)(blockIdx.x % (unsigned)rbph);
+  const int lane = threadIdx.x & 63;
+  uint32_t mx[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    ra[j] = Elt<_Float16>::pack2(cq * to_f32<T>(a[j] & 0xffffu), cq * to_f32<T>(a[j] >> 16));
-    rg[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(g[j] & 0xffffu), -sc.eo),
-                                 ldexpf(to_f32<T>(g[j] >> 16), -sc.eo));
-    rk[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(kk[j] & 0xffffu), -sc.ek),
-                                 ldexpf(to_f32<T>(kk[j] >> 16), -sc.ek));
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t* pt = part + ((size_t)t * BH + bh) * kPreChunks;
+    uint32_t m = 0u;
+    for (int j = lane; j < nchunk; j += 64) m = m > pt[j] ? m : pt[j];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t o2 = (uint32_t)__shfl_xor((int)m, off);
+      m = m > o2 ? m : o2;
+    }
+    mx[t] = m;
   }
-  *reinterpret_cast<u32x4*>(q16 + row * D + col) = ra;
-  *reinterpret_cast<u32x4*>(do16 + row * D + col) = rg;
-  *reinterpret_cast<u32x4*>(k16 + row * D + col) = rk;
-  if (col == 0) {
-    nDs[row] = -ldexpf(Dbuf[row], -(sc.eo + sc.ev));
-    nsh[row] = sc.exact ? -shift[row] / sc.m : -ldexpf(shift[row], -sc.f);
+  if (rb == 0 && threadIdx.x == 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) maxes[(size_t)t * BH + bh] = mx[t];
+  }
+  const Scales sc = bwd_scales_of<D>(mx[0], mx[1], mx[2], mx[3], c);
+  if ((int)threadIdx.x >= RPB * TPR) return;
+  const int col = (int)(threadIdx.x % TPR) * 8;
+  const float cq = ldexpf(sc.exact ? 1.f : c, -sc.eq);
+  for (int it = 0; it < iters; ++it) {
+    const int r = (rb * iters + it) * RPB + (int)(threadIdx.x / TPR);
+    if (r >= N) return;
+    const int64_t row = (int64_t)bh * N + r;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(q + row * D + col);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + col);
+    const u32x4 kk = *reinterpret_cast<const u32x4*>(k + row * D + col);
+    u32x4 ra, rg, rk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ra[j] = Elt<_Float16>::pack2(cq * to_f32<T>(a[j] & 0xffffu), cq * to_f32<T>(a[j] >> 16));
+      rg[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(g[j] & 0xffffu), -sc.eo),
+                                   ldexpf(to_f32<T>(g[j] >> 16), -sc.eo));
+      rk[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(kk[j] & 0xffffu), -sc.ek),
+                                   ldexpf(to_f32<T>(kk[j] >> 16), -sc.ek));
+    }
+    *reinterpret_cast<u32x4*>(q16 + row * D + col) = ra;
+    *reinterpret_cast<u32x4*>(do16 + row * D + col) = rg;
+    *reinterpret_cast<u32x4*>(k16 + row * D + col) = rk;
+    if (col == 0) {
+      nDs[row] = -ldexpf(Dbuf[row], -(sc.eo + sc.ev));
+      nsh[row] = sc.exact ? -shift[row] / sc.m : -ldexpf(shift[row], -sc.f);
+    }
   }
 }
 
@@ -855,8 +887,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
   template __global__ void bwd_dq_kernel<T, D, false, true, false>(BwdParams);          \
   template __global__ void bwd_convert_kernel<T, D>(                               \
       const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*,   \
-      const uint32_t*, float,                                                        \
-      uint16_t*, uint16_t*, uint16_t*, float*, float*, int64_t, int, int);
+      const uint32_t*, int, uint32_t*, float,                                        \
+      uint16_t*, uint16_t*, uint16_t*, float*, float*, int, int, int, int);
 FA_BWD_INSTANTIATE(__bf16, 32)
 FA_BWD_INSTANTIATE(__bf16, 64)
 FA_BWD_INSTANTIATE(__bf16, 96)
@@ -870,7 +902,6 @@ FA_BWD_INSTANTIATE(_Float16, 128)
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t run_bwd(const BwdArgs& a, int stage) {
   hipError_t e = hipSuccess;
-  const int64_t rows = (int64_t)a.B * a.H * a.N;
   const int BH = a.B * a.H;
   const BwdWorkspace w = bwd_workspace_layout(a.B, a.H, a.N, a.d);
   char* ws = static_cast<char*>(a.workspace);
@@ -880,37 +911,41 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   float* nsh = reinterpret_cast<float*>(ws + w.nsh);
   const float c = a.scale * kLog2e;
   uint32_t* maxes = reinterpret_cast<uint32_t*>(ws + w.maxes);
+  uint32_t* part = reinterpret_cast<uint32_t*>(ws + w.part);
   uint16_t* q16 = reinterpret_cast<uint16_t*>(ws + w.q16);
   uint16_t* do16 = reinterpret_cast<uint16_t*>(ws + w.do16);
   uint16_t* k16 = reinterpret_cast<uint16_t*>(ws + w.k16);
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   const uint16_t* dO = static_cast<const uint16_t*>(a.dO);
   if (stage == 0 || stage == 1) {
-    const unsigned row_blocks = (unsigned)((rows * (D / 8) + 255) / 256);
-    hipLaunchKernelGGL(bwd_zero_kernel, dim3((4 * BH + 255) / 256), dim3(256), 0, a.stream,
-                       maxes, 4 * BH);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // row groups per workgroup: up to kPreIter, fewer when that would leave
-    // the grid below about 2048 workgroups (short sequences, few heads), but
-    // never more than 32 workgroups per head (each issues an atomic max on
-    // the head's 4 maxima; more contend: 128 per head took 103 instead of
-    // 72 us at N = 16384, H = 16)
+    // row groups per workgroup of the D pass: enough for a grid of about
+    // 2048 workgroups, and at least enough that a head has at most
+    // kPreChunks workgroups (one partial maximum each)
     constexpr int rpb = 256 / pre_tpr<D>();  // rows per group
     const int64_t groups = (a.N + rpb - 1) / rpb;
-    const int64_t by_head = (groups + 31) / 32, by_grid = (groups * BH + 2047) / 2048;
+    const int64_t by_head = (groups + kPreChunks - 1) / kPreChunks;
+    const int64_t by_grid = (groups * BH + 2047) / 2048;
     int iters = (int)(by_head > by_grid ? by_head : by_grid);
-    iters = iters < 1 ? 1 : (iters > kPreIter ? kPreIter : iters);
+    iters = iters < 1 ? 1 : iters;
     const int pre_rows = rpb * iters;  // rows per workgroup
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D, true>), dim3(BH, (a.N + pre_rows - 1) / pre_rows),
-                       dim3(256), 0, a.stream, static_cast<const uint16_t*>(a.o), dO, a.lse, q,
+    const int nchunk = (a.N + pre_rows - 1) / pre_rows;
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D, true>), dim3(BH, nchunk), dim3(256), 0, a.stream,
+                       static_cast<const uint16_t*>(a.o), dO, a.lse, q,
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), Dbuf,
-                       shift, maxes, a.N, BH, iters);
+                       shift, part, a.N, BH, iters);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_convert_kernel<T, D>), dim3(row_blocks), dim3(256), 0, a.stream, q,
-                       static_cast<const uint16_t*>(a.k), dO, Dbuf, shift, maxes, c, q16, k16,
-                       do16, nDs, nsh, rows, a.N, BH);
+    // convert: row blocks per workgroup so that the grid stays near 4096
+    // workgroups (each reduces the partial maxima once)
+    constexpr int crpb = 256 / (D / 8);  // rows per block
+    const int64_t cblocks = (a.N + crpb - 1) / crpb;
+    int citers = (int)((cblocks * BH) / 4096);
+    citers = citers < 1 ? 1 : (citers > 16 ? 16 : citers);
+    const int rbph = (int)((cblocks + citers - 1) / citers);  // convert workgroups per head
+    hipLaunchKernelGGL((bwd_convert_kernel<T, D>), dim3((unsigned)((int64_t)BH * rbph)),
+                       dim3(256), 0, a.stream, q, static_cast<const uint16_t*>(a.k), dO, Dbuf,
+                       shift, part, nchunk, maxes, c, q16, k16, do16, nDs, nsh, a.N, BH, rbph,
+                       citers);
     e = hipGetLastError();
     if (e != hipSuccess || stage == 1) return e;
   }

@@ -66,14 +66,19 @@ struct BwdArgs {
 //   nDs    f32 [BHN]      -D_i * 2^-(eo+ev)
 //   nsh    f32 [BHN]      -shift_i * 2^-f
 //   maxes  u32 [4][BH]    max |Q|, |K|, |V|, |dO| per (b, h), float bits
+//   part   u32 [4][BH][kPreChunks]  the same per workgroup of the D pass
 //   q16    f16 [BHN d]    c Q * 2^-eq    (c = scale * log2(e))
 //   do16   f16 [BHN d]    dO * 2^-eo
 //   k16    f16 [BHN d]    K * 2^-ek
 // (BHN = B*H*N; eq, ek, ev, eo and f = eq + ek are the per-(b, h)
 // power-of-two exponents that the kernels derive from the maxima.)
 struct BwdWorkspace {
-  size_t D, shift, nDs, nsh, maxes, q16, do16, k16, total;
+  size_t D, shift, nDs, nsh, maxes, part, q16, do16, k16, total;
 };
+
+// Most D-pass workgroups per (b, h): each leaves one partial maximum per
+// tensor, which the convert pass reduces.
+constexpr int kPreChunks = 128;
 
 inline size_t ws_align(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -85,7 +90,8 @@ inline BwdWorkspace bwd_workspace_layout(int64_t B, int64_t H, int64_t N, int64_
   w.nDs = ws_align(w.shift + 4 * bhn);
   w.nsh = ws_align(w.nDs + 4 * bhn);
   w.maxes = ws_align(w.nsh + 4 * bhn);
-  w.q16 = ws_align(w.maxes + 16 * bh);
+  w.part = ws_align(w.maxes + 16 * bh);
+  w.q16 = ws_align(w.part + 16 * bh * kPreChunks);
   w.do16 = ws_align(w.q16 + 2 * bhn * size_t(d));
   w.k16 = ws_align(w.do16 + 2 * bhn * size_t(d));
   w.total = ws_align(w.k16 + 2 * bhn * size_t(d));

@@ -69,17 +69,18 @@ def test_status_strings(lib):
 def ws_formula(B, H, N, d):
     # per query row: D, shift and their scaled negations (4 floats) and the
     # fp16 copies of its q, k and dO rows (6 d bytes); per (b, h): four
-    # maxima; 256-byte alignment of eight regions
-    return 16 * B * H * N + 6 * B * H * N * d + 16 * B * H
+    # maxima and four partial maxima from each of at most 128 D-pass
+    # workgroups; 256-byte alignment of nine regions
+    return 16 * B * H * N + 6 * B * H * N * d + 16 * B * H + 16 * 128 * B * H
 
 
 def test_workspace_is_linear_in_N(lib):
     for B, H, N, d in [(1, 16, 16384, 64), (2, 3, 1000, 128), (1, 1, 1, 64)]:
         got = lib.fa_bwd_workspace_size(B, H, N, d)
-        assert ws_formula(B, H, N, d) <= got < ws_formula(B, H, N, d) + 8 * 256
+        assert ws_formula(B, H, N, d) <= got < ws_formula(B, H, N, d) + 9 * 256
         assert got % 256 == 0
     a, b = lib.fa_bwd_workspace_size(1, 16, 8192, 64), lib.fa_bwd_workspace_size(1, 16, 16384, 64)
-    assert abs(b - 2 * a) <= 8 * 256
+    assert abs(b - 2 * a) <= 16 * 128 * 16 + 9 * 256
     assert lib.fa_bwd_workspace_size(2, 2, 256, 64) == WS
     assert lib.fa_bwd_workspace_size(0, 1, 1, 64) == 0
 
@@ -87,7 +88,7 @@ def test_workspace_is_linear_in_N(lib):
 # Fake, never-dereferenced, 16-byte aligned "device" addresses: validation
 # rejects every call below before anything touches them.
 P = 0x100000
-WS = 409856  # fa_bwd_workspace_size(2, 2, 256, 64), checked below
+WS = 418048  # fa_bwd_workspace_size(2, 2, 256, 64), checked below
 F16, BF16, F32 = 1, 2, 0
 
 
