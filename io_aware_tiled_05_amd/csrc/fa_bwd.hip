@@ -389,26 +389,36 @@ __device__ __forceinline__ int list_blocks(const uint8_t* m, int stride, int w0,
 // T is the input/output type; the products run on the scaled fp16 operands
 // described at the top of this file.
 // DROP: dropout on P (dV uses P M / (1 - p), dS = P (dP M / (1 - p) - D))
+// LDS of one dK/dV workgroup: double-buffered Q and dO tiles and their row
+// terms, and the block-sparse list
+template <int D, bool SPARSE>
+struct DkdvLds {
+  __attribute__((aligned(16))) uint16_t q0[kBQ * D], q1[kBQ * D], o0[kBQ * D], o1[kBQ * D];
+  __attribute__((aligned(16))) float l0[kBQ], l1[kBQ], d0[kBQ], d1[kBQ];
+  int list[SPARSE ? kListMax : 1];
+};
+
+// workgroup `wg` of the dK/dV grid
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SPARSE>& lds) {
   constexpr int KS = D / 16, DB = D / 32, TILE = kBQ * D, NW = 4;
   typedef _Float16 TI;
   typedef typename Elt<TI>::vec8 vec8;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ0[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ1[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sO0[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sO1[TILE];
-  __shared__ __attribute__((aligned(16))) float sL0[kBQ];
-  __shared__ __attribute__((aligned(16))) float sL1[kBQ];
-  __shared__ __attribute__((aligned(16))) float sD0[kBQ];
-  __shared__ __attribute__((aligned(16))) float sD1[kBQ];
-  __shared__ int sList[SPARSE ? kListMax : 1];
+  uint16_t* const sQ0 = lds.q0;
+  uint16_t* const sQ1 = lds.q1;
+  uint16_t* const sO0 = lds.o0;
+  uint16_t* const sO1 = lds.o1;
+  float* const sL0 = lds.l0;
+  float* const sL1 = lds.l1;
+  float* const sD0 = lds.d0;
+  float* const sD1 = lds.d1;
+  int* const sList = lds.list;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5, sub = lane & 15, g4 = lane >> 4;
   int rank, bh;
-  map_workgroup(blockIdx.x, p.ntiles, p.BH, p.period, &rank, &bh);
+  map_workgroup(wg, p.ntiles, p.BH, p.period, &rank, &bh);
   const int kt = rank;  // causal: the lowest key tiles see the most queries, so go first
   const int b = bh / p.H, N = p.N;
   const size_t base = (size_t)bh * N * D;
@@ -656,23 +666,32 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
 // ---------------------------------------------------------------------------
 // DROP: dS = P (dP M / (1 - p) - D); dP starts from 0 and D enters after
 // the mask
+// LDS of one dQ workgroup: double-buffered K and V tiles and the
+// block-sparse list
+template <int D, bool SPARSE>
+struct DqLds {
+  __attribute__((aligned(16))) uint16_t k0[kBC * D], k1[kBC * D], v0[kBC * D], v1[kBC * D];
+  int list[SPARSE ? kListMax : 1];
+};
+
+// workgroup `wg` of the dQ grid
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE>& lds) {
   constexpr int KS = D / 16, DB = D / 32, TILE = kBC * D, NW = 4;
   typedef _Float16 TI;
   typedef typename Elt<TI>::vec8 hvec8;
   typedef typename Elt<T>::vec8 vec8;
-  __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
-  __shared__ int sList[SPARSE ? kListMax : 1];
+  uint16_t* const sK0 = lds.k0;
+  uint16_t* const sK1 = lds.k1;
+  uint16_t* const sV0 = lds.v0;
+  uint16_t* const sV1 = lds.v1;
+  int* const sList = lds.list;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5, sub = lane & 15, g4 = lane >> 4;
   int rank, bh;
-  map_workgroup(blockIdx.x, p.ntiles, p.BH, p.period, &rank, &bh);
+  map_workgroup(wg, p.ntiles, p.BH, p.period, &rank, &bh);
   const int qt = CAUSAL ? p.ntiles - 1 - rank : rank;  // longest rows first
   const int b = bh / p.H, N = p.N;
   const size_t base = (size_t)bh * N * D;
@@ -869,6 +888,38 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
   }
 }
 
+// The two gradient kernels as separate launches (fa_bwd_stage) ...
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParams p) {
+  __shared__ DkdvLds<D, SPARSE> lds;
+  bwd_dkdv_body<T, D, CAUSAL, SPARSE, DROP>(p, (int)blockIdx.x, lds);
+}
+
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams p) {
+  __shared__ DqLds<D, SPARSE> lds;
+  bwd_dq_body<T, D, CAUSAL, SPARSE, DROP>(p, (int)blockIdx.x, lds);
+}
+
+// ... and as one launch (fa_bwd): the dK/dV and dQ kernels need only what
+// the D pass wrote, not each other, so the first ntiles * BH workgroups
+// take dK/dV and the rest dQ, and dQ workgroups start while the last,
+// longest dK/dV workgroups still run (short sequences leave most compute
+// units idle in each kernel's tail).  The two LDS layouts share one buffer.
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_fused_kernel(BwdParams p) {
+  static_assert(kBKV == kBR, "one tile count for both parts of the grid");
+  __shared__ union {
+    DkdvLds<D, SPARSE> kv;
+    DqLds<D, SPARSE> q;
+  } lds;
+  const int n = p.ntiles * p.BH;
+  if ((int)blockIdx.x < n)
+    bwd_dkdv_body<T, D, CAUSAL, SPARSE, DROP>(p, (int)blockIdx.x, lds.kv);
+  else
+    bwd_dq_body<T, D, CAUSAL, SPARSE, DROP>(p, (int)blockIdx.x - n, lds.q);
+}
+
 // Every kernel the launcher below can select (the host pass of this compiler
 // otherwise leaves some kernel-template launch stubs undefined).
 #define FA_BWD_INSTANTIATE(T, D)                                                  \
@@ -884,7 +935,12 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
   template __global__ void bwd_dq_kernel<T, D, false, false, false>(BwdParams);    \
   template __global__ void bwd_dq_kernel<T, D, true, false, true>(BwdParams);      \
   template __global__ void bwd_dq_kernel<T, D, false, false, true>(BwdParams);     \
-  template __global__ void bwd_dq_kernel<T, D, false, true, false>(BwdParams);          \
+  template __global__ void bwd_dq_kernel<T, D, false, true, false>(BwdParams);     \
+  template __global__ void bwd_fused_kernel<T, D, true, false, false>(BwdParams);  \
+  template __global__ void bwd_fused_kernel<T, D, false, false, false>(BwdParams); \
+  template __global__ void bwd_fused_kernel<T, D, true, false, true>(BwdParams);   \
+  template __global__ void bwd_fused_kernel<T, D, false, false, true>(BwdParams);  \
+  template __global__ void bwd_fused_kernel<T, D, false, true, false>(BwdParams);  \
   template __global__ void bwd_convert_kernel<T, D>(                               \
       const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*,   \
       const uint32_t*, int, uint32_t*, float,                                        \
@@ -977,14 +1033,20 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   p.period = (FA_BWD_SNAKE && CAUSAL) ? snake_period(p.BH) : 0;
   p.drop = a.drop;
 
-  if (stage == 0 || stage == 2) {
+  if (stage == 0) {
+    p.ntiles = (a.N + kBKV - 1) / kBKV;
+    hipLaunchKernelGGL((bwd_fused_kernel<T, D, CAUSAL, SPARSE, DROP>),
+                       dim3(2 * p.ntiles * p.BH), dim3(256), 0, a.stream, p);
+    return hipGetLastError();
+  }
+  if (stage == 2) {
     p.ntiles = (a.N + kBKV - 1) / kBKV;
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(p.ntiles * p.BH),
                        dim3(256), 0, a.stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stage == 0 || stage == 3) {
+  if (stage == 3) {
     p.ntiles = (a.N + kBR - 1) / kBR;
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(p.ntiles * p.BH),
                        dim3(256), 0, a.stream, p);

@@ -1,0 +1,84 @@
+"""The backward as one call (fa_bwd: the D pass, then one launch that runs the
+dK/dV and dQ workgroups together) and as its three stages launched one at a
+time (fa_bwd_stage) must give the same gradients bit for bit: every output
+element is computed by the same arithmetic in both.  The one-call form is
+checked against the fp64 oracle by test_parity_bwd.py; one case here is
+checked against it too, through the staged form.
+"""
+
+import numpy as np
+import pytest
+
+from helpers import TOL, assert_close, to_dev, to_np
+from oracle import attention_bwd
+from workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import io_aware_tiled_05_amd as fa
+    fa.load()
+    return fa
+
+
+def both(fa, x, dtype, causal=False, key_len=None, block_mask=None):
+    import torch
+    q, k, v, dO = (to_dev(x[n], dtype) for n in ("q", "k", "v", "dO"))
+    s = x["scale"]
+    B, H, N, d = q.shape
+    kl = None if key_len is None else torch.from_numpy(key_len.astype(np.int32)).cuda()
+    bm = None if block_mask is None else torch.from_numpy(block_mask).cuda()
+    if bm is not None:
+        o, lse = fa.fa_fwd_blocksparse(q, k, v, bm, scale=s)
+        one = fa.fa_bwd_blocksparse(q, k, v, o, lse, dO, bm, scale=s)
+    else:
+        o, lse = fa.fa_fwd(q, k, v, scale=s, causal=causal, key_len=kl)
+        one = fa.fa_bwd(q, k, v, o, lse, dO, scale=s, causal=causal, key_len=kl)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d) // 4, dtype=torch.float32,
+                     device=q.device)
+    for st in (fa.FA_BWD_STAGE_D, fa.FA_BWD_STAGE_DKDV, fa.FA_BWD_STAGE_DQ):
+        fa.fa_bwd_stage(st, q, k, v, o, lse, dO, dq, dk, dv, ws, scale=s, causal=causal,
+                        key_len=kl, block_mask=bm)
+    torch.cuda.synchronize()
+    return one, (dq, dk, dv)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("N", [7, 129, 700])
+@pytest.mark.parametrize("mask", ["none", "causal", "pad"])
+def test_one_call_equals_stages(fa, dtype, d, N, mask):
+    x = make_inputs(Workload("stages", 2, 3, N, d, dtype, seed=21))
+    key_len = None
+    if mask == "pad":
+        key_len = np.random.default_rng(N + d).integers(1, N, size=2, endpoint=True)
+    one, staged = both(fa, x, dtype, causal=mask == "causal", key_len=key_len)
+    print(f"[bwd one call vs stages {dtype} d={d} N={N} {mask}]")
+    for name, a, b in zip(("dq", "dk", "dv"), one, staged):
+        assert bool((a == b).all()), f"{name} differs between fa_bwd and fa_bwd_stage"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_one_call_equals_stages_blocksparse(fa, dtype):
+    N = 700
+    nb = (N + 127) // 128
+    bm = (np.random.default_rng(3).random((nb, nb)) < 0.5).astype(np.uint8)
+    np.fill_diagonal(bm, 1)
+    bm[1, :] = 0  # a block row without keys
+    x = make_inputs(Workload("stages", 1, 2, N, 64, dtype, seed=22))
+    one, staged = both(fa, x, dtype, block_mask=bm)
+    print(f"[bwd one call vs stages block-sparse {dtype} N={N}]")
+    for name, a, b in zip(("dq", "dk", "dv"), one, staged):
+        assert bool((a == b).all()), f"{name} differs between fa_bwd and fa_bwd_stage"
+
+
+def test_stages_against_oracle(fa):
+    x = make_inputs(Workload("stages", 2, 2, 300, 64, "bf16", seed=23))
+    _, staged = both(fa, x, "bf16", causal=True)
+    ref = attention_bwd(x["q"], x["k"], x["v"], x["dO"], x["scale"], causal=True)
+    print("[bwd stages vs oracle bf16 d=64 N=300 causal]")
+    for name, got, want in zip(("dq", "dk", "dv"), staged, ref):
+        assert_close(name, to_np(got), want, TOL["bf16"])
