@@ -103,8 +103,11 @@ def measured_traffic(kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
+# bwd_fused: the dK/dV and dQ workgroups of fa_bwd in one launch (the timed
+# step); bwd_dkdv and bwd_dq: the same bodies launched one at a time (the
+# instrumented loop)
 KERNEL_KEYS = (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"),
-               ("bwd_pre_kernel", "bwd_pre"), ("bwd_zero_kernel", "bwd_pre"),
+               ("bwd_fused_kernel", "bwd_fused"), ("bwd_pre_kernel", "bwd_pre"),
                ("bwd_convert_kernel", "bwd_pre"), ("fwd_kernel", "fwd"))
 
 
@@ -144,7 +147,7 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, cop
             key = kernel_key(name)
             if key is None:
                 continue
-            # kernels of one key (the three launches of the D pass) add up
+            # kernels of one key (the two launches of the D pass) add up
             per.setdefault(key, {}).setdefault(field, {})[name] = sum(vals) / len(vals) * 1024 * fac
     kernels = {}
     for key, d in per.items():
@@ -387,7 +390,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # about 100 ms of work at the default workload: with 5 warm-up steps
+    # (12 ms) the first timed loop still ran about 3 % slow
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="long_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV",
