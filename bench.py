@@ -62,12 +62,16 @@ PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12    # 2516.6 dense bf16/fp16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
+# the sources the forward and 16-bit backward kernels are built from
+TRAFFIC_SOURCES = ("fa_api.cpp", "fa_bwd.hip", "fa_device.h", "fa_fwd.hip", "fa_internal.h")
+
+
 def source_hash() -> str:
-    """Hash of the HIP sources; HBM-traffic figures are only reported while
-    the kernels still match the build they were measured on."""
+    """Hash of the sources of the measured kernels; HBM-traffic figures are
+    only reported while those still match the build they were measured on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "io_aware_tiled_05_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in TRAFFIC_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
