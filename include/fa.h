@@ -99,8 +99,9 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 /* Backward with recomputation ([ODP "The key idea"]; [DEC "The Hardware
  * Picture: Why Tiling Wins"]): the probabilities are rebuilt on-chip from
  * q, k and lse; nothing of size N x N is stored.  Launches on `stream`:
- * D = rowsum(dO * O) with the operand copies; dK/dV (one workgroup per key tile);
- * dQ (one workgroup per query tile).  Deterministic: no atomics.
+ * D = rowsum(dO * O) with the operand copies; then dK/dV (one workgroup per
+ * key tile) and dQ (one workgroup per query tile), for 16-bit inputs as one
+ * launch whose grid holds both.  Deterministic: no atomics.
  *   o, lse  : the forward's outputs for the same inputs and mask
  *   dO      : upstream gradient [B][H][N][d], dtype
  *   dq,dk,dv: outputs [B][H][N][d], dtype (overwritten)
@@ -139,11 +140,13 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v,
  *   stage FA_BWD_STAGE_D    : the workspace: D_i = sum_c dO_ic O_ic, the
  *                             softmax shift, the per-(b, h) maxima and the
  *                             scaled 16-bit copies of q, k and dO
- *                             (three launches; fp32: D and the shift only,
+ *                             (two launches; fp32: D and the shift only,
  *                             one launch)
  *   stage FA_BWD_STAGE_DKDV : dk, dv (reads the workspace written by stage 1)
  *   stage FA_BWD_STAGE_DQ   : dq     (reads the workspace written by stage 1)
- * Running stages 1, 2, 3 in this order on one stream equals fa_bwd.  The
+ * Running stages 1, 2, 3 in this order on one stream gives fa_bwd's results
+ * bit for bit (fa_bwd itself runs the 16-bit dK/dV and dQ workgroups in one
+ * launch; stages 2 and 3 launch them separately).  The
  * arguments are those of fa_bwd; block_mask non-NULL selects the
  * block-sparse variant (then causal must be 0, key_len NULL and block_size
  * 128; block_size is ignored otherwise).  Pointers a stage does not touch

@@ -146,7 +146,8 @@ inline DecodeSplit decode_split(int64_t B, int64_t H, int64_t Nq, int64_t Nk, in
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_fwd(const FwdArgs& a);
-// stage 0: all three launches; 1: D only; 2: dK/dV only; 3: dQ only
+// stage 0: the whole backward (16-bit: the D pass, then one launch that runs
+// the dK/dV and dQ workgroups together); 1: D only; 2: dK/dV only; 3: dQ only
 hipError_t launch_bwd(const BwdArgs& a, int stage);
 // fp32 inputs (dense, causal, key padding; no block mask); same stages
 hipError_t launch_bwd_f32(const BwdArgs& a, int stage);
