@@ -99,3 +99,49 @@ def test_largest_accepted_size(fa):
     assert np.all(err_v <= tol_v)
     del q, k, v, dO, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("Nq", [1, 4])
+def test_decode_largest_accepted_size(fa, Nq):
+    """fa_decode with Nk = (2^31 - 1) // 64 cached keys (the largest the C
+    ABI accepts): q = 0, so every key has weight 1 / Nk (any K), O is the
+    mean of all V rows and lse = ln Nk.  V is a ramp in the key index (even
+    columns rising, odd falling, bf16-rounded), so a key range read from the
+    wrong place or skipped moves the mean; the expected mean is summed in
+    fp64 from the same bf16 tensor, and lse pins the count of keys (fp32:
+    1e-5 is about 335 keys of 33.5 million)."""
+    import math
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    if props.total_memory < 32 * 2 ** 30:
+        pytest.skip("needs about 10 GiB of device memory")
+    dev = torch.device("cuda:0")
+    Nk = N
+    print(f"[decode max size: B=1 H=1 Nq={Nq} Nk={Nk} d={D} bf16, q = 0]", flush=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(32)
+    k = torch.randn((1, 1, Nk, D), device=dev, dtype=torch.bfloat16, generator=g)
+    ramp = torch.arange(Nk, device=dev, dtype=torch.float32) / Nk
+    v = torch.empty((1, 1, Nk, D), device=dev, dtype=torch.bfloat16)
+    v[0, 0, :, 0::2] = ramp[:, None].to(torch.bfloat16)
+    v[0, 0, :, 1::2] = (1.0 - ramp)[:, None].to(torch.bfloat16)
+    del ramp
+    q = torch.zeros((1, 1, Nq, D), device=dev, dtype=torch.bfloat16)
+    o, lse = fa.fa_decode(q, k, v, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    mean = torch.zeros(D, dtype=torch.float64, device=dev)
+    step = 1 << 22
+    for r0 in range(0, Nk, step):
+        mean += v[0, 0, r0:r0 + step].to(torch.float64).sum(dim=0)
+    mean = (mean / Nk).cpu().numpy()
+    O = o[0, 0].float().cpu().numpy().astype(np.float64)
+    L = lse[0, 0].cpu().numpy().astype(np.float64)
+    for i in range(Nq):
+        assert_close(f"O row {i}", O[i], mean, TOL["bf16"])
+    err_l = np.abs(L - math.log(Nk)).max()
+    print(f"  lse: max|err| = {err_l:.3e} (tol 1e-05)", flush=True)
+    assert err_l <= 1e-5
+    # the rounded mean itself: half of the columns near 0.5 either way
+    assert np.abs(O - mean[None]).max() <= 2.0 ** -9 + 1e-6
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
