@@ -514,10 +514,11 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParamsF32 p) {
       FwdParams);                                                                            \
   template __global__ void fwd_kernel<T, D, 4, 32, true, false, true>(FwdParams);            \
   template __global__ void fwd_kernel<T, D, 4, 32, false, false, true>(FwdParams);
-// the 32-query dense kernels that small grids select where 64 is the default
+// the two-wave, 32-query dense kernels that small grids select where 64 is
+// the default
 #define FA_FWD_INSTANTIATE_SMALL(T, D)                                                        \
-  template __global__ void fwd_kernel<T, D, 4, 32, true, false, false>(FwdParams);           \
-  template __global__ void fwd_kernel<T, D, 4, 32, false, false, false>(FwdParams);
+  template __global__ void fwd_kernel<T, D, 2, 32, true, false, false>(FwdParams);           \
+  template __global__ void fwd_kernel<T, D, 2, 32, false, false, false>(FwdParams);
 
 #define FA_FWD_INSTANTIATE_D(D)                                                               \
   FA_FWD_INSTANTIATE(__bf16, D)                                                              \
@@ -537,10 +538,11 @@ FA_FWD_INSTANTIATE_SMALL(_Float16, 64)
 #undef FA_FWD_INSTANTIATE_D
 #undef FA_FWD_INSTANTIATE
 
-template <typename T, int D, int QW, bool CAUSAL, bool SPARSE, bool DROP>
+template <typename T, int D, int QW, bool CAUSAL, bool SPARSE, bool DROP, int NWD = 4>
 hipError_t launch_fwd_kernel(const FwdArgs& a) {
-  // block-sparse workgroups cover exactly one 128-query mask row
-  constexpr int NW = SPARSE ? 128 / QW : 4;
+  // block-sparse workgroups cover exactly one 128-query mask row; dense
+  // ones NWD waves
+  constexpr int NW = SPARSE ? 128 / QW : NWD;
   constexpr int BR = NW * QW;
   FwdParams p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -569,9 +571,11 @@ hipError_t launch_fwd_kernel(const FwdArgs& a) {
 // each K/V tile of a 128-query mask row: measured 3-5 % faster than two
 // waves of 64 queries).  Dense 64-query waves at d <= 64 halve the LDS
 // reads per MFMA, but when their grid has fewer workgroups than the GPU has
-// compute units, 32-query waves (twice the workgroups) finish sooner
-// (causal B = 8, H = 12, N = 1024: 192 -> 384 workgroups, 45.6 -> 37.0 us;
-// with 256 workgroups on 256 CUs, 64-query waves stay ahead).
+// compute units, workgroups of two 32-query waves (four times the
+// workgroups, each causal pair of equal work) finish sooner (causal B = 8,
+// H = 12, N = 1024: 192 -> 768 workgroups, 45.6 -> 33.8 us; four waves of
+// 32 queries, 384 workgroups: 37.0 us; with 256 workgroups on 256 CUs,
+// 64-query waves stay ahead).
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t run_fwd(const FwdArgs& a) {
   constexpr int QW = (DROP || SPARSE) ? 32 : FwdShape<D>::QW;
@@ -579,7 +583,7 @@ hipError_t run_fwd(const FwdArgs& a) {
     const int nqt = (a.N + 4 * QW - 1) / (4 * QW);
     const long wgs = (long)(CAUSAL ? (nqt + 1) / 2 : nqt) * a.B * a.H;
     const int cus = device_cu_count();
-    if (cus > 0 && wgs < cus) return launch_fwd_kernel<T, D, 32, CAUSAL, SPARSE, DROP>(a);
+    if (cus > 0 && wgs < cus) return launch_fwd_kernel<T, D, 32, CAUSAL, SPARSE, DROP, 2>(a);
   }
   return launch_fwd_kernel<T, D, QW, CAUSAL, SPARSE, DROP>(a);
 }
