@@ -4,14 +4,18 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step = one forward (fa_fwd) plus one backward (fa_bwd: D = rowsum(dO * O)
-and the fp16 operand copies, dK/dV, dQ) over the whole batch, inputs already
-resident in HBM.  K steps are timed between two synchronisations with HIP
-events recorded on the stream the kernels run on (torch's current stream,
-which the binding passes to the library): that is `value` and ms_per_step.
-K more steps then run the backward as its three stages (fa_bwd_stage) with
-an event after every launch, which gives each kernel's average duration
-(kernel_ms, roofline); those events add a few microseconds between launches,
-so that loop is reported separately (ms_per_step_with_kernel_events).
+and the fp16 operand copies, then one launch holding the dK/dV and dQ
+workgroups) over the whole batch, inputs already resident in HBM.  K steps
+are timed between two synchronisations with HIP events recorded on the
+stream the kernels run on (torch's current stream, which the binding passes
+to the library): that is `value` and ms_per_step.  K more steps then run the
+same launches with an event after each (fa_fwd, then fa_bwd as its two
+stages: FA_BWD_STAGE_D and FA_BWD_STAGE_GRADS, which is exactly fa_bwd's
+launch sequence), which gives each kernel's average duration (kernel_ms,
+roofline); those events add a few microseconds between launches, so that
+loop is reported separately (ms_per_step_with_kernel_events).  A third loop
+launches the dK/dV and dQ workgroups as separate kernels (stages DKDV, DQ)
+for their individual times (kernel_ms_staged; not part of the step).
 
 Metric: attention fwd+bwd TFLOPS with the algorithmic FLOP count: 4 d flops
 per visible (query, key) pair forward (Q K^T and P V) and 10 d backward
@@ -265,7 +269,7 @@ def bench_workload(args, w, fa, torch, np, with_cpu):
     if not 0.0 <= drop_p < 1.0:
         raise SystemExit("--dropout must be in [0, 1)")
 
-    def step(ev=None):
+    def step(ev=None, stages=None):
         if ev is not None:
             ev[0].record(stream)
         if ev is None and drop_p == 0.0:
@@ -295,7 +299,7 @@ def bench_workload(args, w, fa, torch, np, with_cpu):
             fa.fa_fwd(q, k, v, scale=scale, causal=causal, key_len=kl, out=o, lse=lse)
         if ev is not None:
             ev[1].record(stream)
-        for i, st in enumerate((fa.FA_BWD_STAGE_D, fa.FA_BWD_STAGE_DKDV, fa.FA_BWD_STAGE_DQ)):
+        for i, st in enumerate(stages):
             fa.fa_bwd_stage(st, q, k, v, o, lse, dO, dq, dk, dv, ws, scale=scale, causal=causal,
                             key_len=kl, block_mask=bm)
             if ev is not None:
@@ -317,36 +321,53 @@ def bench_workload(args, w, fa, torch, np, with_cpu):
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(end) / args.steps
+    # the step's own launches, an event after each: the forward, the D
+    # stage and the one-launch dK/dV + dQ stage (= fa_bwd)
+    step_stages = (fa.FA_BWD_STAGE_D, fa.FA_BWD_STAGE_GRADS)
     start2.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], step_stages)
     end2.record(stream)
     torch.cuda.synchronize()
     ms_step_ev = start2.elapsed_time(end2) / args.steps
-    names = ("fwd", "bwd") if drop_p > 0.0 else ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+    names = ("fwd", "bwd") if drop_p > 0.0 else ("fwd", "bwd_pre", "bwd_fused")
     kms = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
            for j, nm in enumerate(names)}
+    kms_staged = None
+    if drop_p == 0.0:
+        # the dK/dV and dQ workgroups as separate launches (not the step)
+        for i in range(args.steps):
+            step(evs[i], (fa.FA_BWD_STAGE_D, fa.FA_BWD_STAGE_DKDV, fa.FA_BWD_STAGE_DQ))
+        torch.cuda.synchronize()
+        kms_staged = {nm: round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])), 4)
+                      for j, nm in ((2, "bwd_dkdv"), (3, "bwd_dq"))}
 
     P = visible_pairs(w, x)
     fwd_flops, bwd_flops = 4 * d * P, 10 * d * P
     total_tflops = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
-    bwd_ms = kms["bwd"] if drop_p > 0.0 else kms["bwd_pre"] + kms["bwd_dkdv"] + kms["bwd_dq"]
+    bwd_ms = kms["bwd"] if drop_p > 0.0 else kms["bwd_pre"] + kms["bwd_fused"]
     fwd_tflops = fwd_flops / (kms["fwd"] * 1e-3) / 1e12
     bwd_tflops = bwd_flops / (bwd_ms * 1e-3) / 1e12
 
-    # dominant kernel and its algorithmic work per launch:
-    #   fwd 4 d/pair; dK/dV 8 d/pair (S, dP, dV, dK); dQ 2 d/pair (the dQ
-    #   product; its recomputed S and dP repeat work already counted)
-    #   (with dropout the backward is timed as one: 10 d/pair)
-    algo = {"fwd": 4 * d * P, "bwd_dkdv": 8 * d * P, "bwd_dq": 2 * d * P, "bwd": 10 * d * P}
-    dom = max(kms, key=lambda nm: kms[nm] if nm in algo else 0.0)
-    achieved = algo[dom] / (kms[dom] * 1e-3) / 1e12
-    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+    # algorithmic work per launch of each kernel of the step:
+    #   fwd 4 d/pair (Q K^T, P V); bwd_fused 10 d/pair (the recomputed S,
+    #   dP, dV, dK, dQ: the one launch of dK/dV and dQ workgroups)
+    #   (with dropout the backward is timed as one call: 10 d/pair)
+    algo = {"fwd": 4 * d * P, "bwd_fused": 10 * d * P, "bwd": 10 * d * P}
+    # traffic: the committed counters were taken on the long causal workload
+    with_traffic = drop_p == 0.0 and w.name == "long_causal"
+
+    def roofline_of(kern):
+        achieved = algo[kern] / (kms[kern] * 1e-3) / 1e12
+        return {"kernel": kern, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                # the committed counters were taken on the long causal workload
-                "traffic": measured_traffic(dom) if drop_p == 0.0 and w.name == "long_causal"
-                else None}
+                "traffic": measured_traffic(kern) if with_traffic else None}
+
+    # the dominant kernel of the step, and the forward beside it
+    dom = max((nm for nm in kms if nm in algo), key=lambda nm: kms[nm])
+    roofline = roofline_of(dom)
+    roofline_fwd = roofline_of("fwd")
 
     metric = "attention fwd+bwd TFLOPS & % MFMA peak, bf16 d=64, N=1K-16K, 1 GPU"
     if d != 64:
@@ -383,8 +404,10 @@ def bench_workload(args, w, fa, torch, np, with_cpu):
         "fwd_frac_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
         "bwd_frac_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {nm: round(v, 4) for nm, v in kms.items()},
+        "kernel_ms_staged": kms_staged,
         "wall_s_timed": round(t_wall, 3),
         "roofline": roofline,
+        "roofline_fwd": roofline_fwd,
         "cpu_baseline": cpu_baseline(x, w) if with_cpu else None,
     }
     return out

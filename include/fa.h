@@ -126,7 +126,16 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
                        const uint8_t* block_mask, int block_size, int dtype,
                        void* stream);
 
-/* Block-sparse backward: fa_bwd restricted to the selected blocks. */
+/* Block-sparse backward ([DEC "The Passage", block-sparse extension; "Key
+ * Vocabulary", block-sparse attention], with the recomputation of fa_bwd:
+ * [ODP "The key idea"]): fa_bwd's gradients of the block-sparse forward,
+ * with every tile product restricted to the selected blocks — dK/dV
+ * workgroups walk the selected blocks of their key column, dQ workgroups
+ * those of their query row; unselected blocks are skipped, never masked.
+ *   o, lse    : fa_fwd_blocksparse's outputs for the same inputs and mask
+ *   block_mask, block_size: as fa_fwd_blocksparse (block_size must be 128)
+ * Other arguments, the workspace and the errors as fa_bwd; dtype FA_F16 or
+ * FA_BF16 (FA_F32: FA_ERR_UNSUPPORTED).  Deterministic: no atomics. */
 int fa_bwd_blocksparse(const void* q, const void* k, const void* v,
                        const void* o, const float* lse, const void* dO,
                        void* dq, void* dk, void* dv, int B, int H, int N,
@@ -134,9 +143,9 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v,
                        int block_size, void* workspace, size_t workspace_bytes,
                        int dtype, void* stream);
 
-/* The three stages of fa_bwd / fa_bwd_blocksparse, one at a time, for
- * callers that schedule them separately (to time each kernel, or to place
- * them on different streams with their own events).
+/* The stages of fa_bwd / fa_bwd_blocksparse, one at a time, for callers
+ * that schedule them separately (to time each kernel, or to place them on
+ * different streams with their own events).
  *   stage FA_BWD_STAGE_D    : the workspace: D_i = sum_c dO_ic O_ic, the
  *                             softmax shift, the per-(b, h) maxima and the
  *                             scaled 16-bit copies of q, k and dO
@@ -144,14 +153,23 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v,
  *                             one launch)
  *   stage FA_BWD_STAGE_DKDV : dk, dv (reads the workspace written by stage 1)
  *   stage FA_BWD_STAGE_DQ   : dq     (reads the workspace written by stage 1)
- * Running stages 1, 2, 3 in this order on one stream gives fa_bwd's results
- * bit for bit (fa_bwd itself runs the 16-bit dK/dV and dQ workgroups in one
- * launch; stages 2 and 3 launch them separately).  The
+ *   stage FA_BWD_STAGE_GRADS: dk, dv and dq exactly as fa_bwd launches them
+ *                             after stage 1 (16-bit: one launch whose grid
+ *                             holds the dK/dV and the dQ workgroups; fp32:
+ *                             stages 2 and 3)
+ * Running stages 1, 2, 3 in this order on one stream, or stages 1 and 4,
+ * gives fa_bwd's results bit for bit: stage 1 followed by stage 4 is
+ * exactly the launch sequence of fa_bwd.  The
  * arguments are those of fa_bwd; block_mask non-NULL selects the
  * block-sparse variant (then causal must be 0, key_len NULL and block_size
  * 128; block_size is ignored otherwise).  Pointers a stage does not touch
  * must still be valid arguments.  An unknown stage is FA_ERR_INVALID. */
-enum { FA_BWD_STAGE_D = 1, FA_BWD_STAGE_DKDV = 2, FA_BWD_STAGE_DQ = 3 };
+enum {
+  FA_BWD_STAGE_D = 1,
+  FA_BWD_STAGE_DKDV = 2,
+  FA_BWD_STAGE_DQ = 3,
+  FA_BWD_STAGE_GRADS = 4
+};
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v,
                  const void* o, const float* lse, const void* dO, void* dq,
                  void* dk, void* dv, int B, int H, int N, int d, float scale,

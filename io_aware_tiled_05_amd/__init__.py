@@ -12,6 +12,7 @@ from __future__ import annotations
 import math
 
 from ._lib import (FA_BF16, FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ,  # noqa: F401
+                   FA_BWD_STAGE_GRADS,  # noqa: F401
                    FA_ERR_HIP, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_F16,  # noqa: F401
                    FA_F32, FA_OK, FaError, check, load)
 
@@ -169,7 +170,7 @@ def fa_bwd_blocksparse(q, k, v, o, lse, dO, block_mask, block_size=128, scale=No
 
 def fa_bwd_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, workspace, scale=None, causal=False,
                  key_len=None, block_mask=None, block_size=128, stream=None):
-    """One launch of the backward (FA_BWD_STAGE_D, _DKDV or _DQ); outputs and
+    """One stage of the backward (FA_BWD_STAGE_D, _DKDV, _DQ or _GRADS); outputs and
     workspace are caller-allocated; see include/fa.h (fa_bwd_stage)."""
     _check_qkv(q, k, v, o, dO, dq, dk, dv)
     B, H, N, d = q.shape

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
-FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ = 1, 2, 3
+FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ, FA_BWD_STAGE_GRADS = 1, 2, 3, 4
 
 # (name, restype, argtypes) for every function in include/fa.h
 _P, _I, _F, _SZ = C.c_void_p, C.c_int, C.c_float, C.c_size_t

@@ -47,6 +47,9 @@ int make_dropout(float p, uint64_t seed, uint32_t offset, fa::Dropout* out) {
   const double t = std::floor((double)p * 65536.0);  // 16-bit draws
   dr.thresh = t >= 65535.0 ? 65535u : (uint32_t)t;
   dr.rinv = (float)(1.0 / (1.0 - (double)p));
+  int e = 0;  // smallest e with 2^e >= rinv
+  while (e < 30 && std::ldexp(1.0, e) < (double)dr.rinv) ++e;
+  dr.rexp = e;
   dr.k0 = (uint32_t)(seed & 0xFFFFFFFFu);
   dr.k1 = (uint32_t)(seed >> 32);
   dr.offset = offset;
@@ -144,7 +147,7 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  int N, int d, float scale, int causal, const int32_t* key_len,
                  const uint8_t* block_mask, int block_size, void* workspace,
                  size_t workspace_bytes, int dtype, void* stream) {
-  if (stage < FA_BWD_STAGE_D || stage > FA_BWD_STAGE_DQ) return FA_ERR_INVALID;
+  if (stage < FA_BWD_STAGE_D || stage > FA_BWD_STAGE_GRADS) return FA_ERR_INVALID;
   if (block_mask) {
     if (causal || key_len) return FA_ERR_INVALID;
     if (block_size != 128) return block_size < 1 ? FA_ERR_INVALID : FA_ERR_UNSUPPORTED;

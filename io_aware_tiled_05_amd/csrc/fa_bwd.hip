@@ -43,7 +43,9 @@
 // The power-of-two exponents keep every operand in fp16 range (max |dO'|
 // in [2^3, 2^4), |V'| in [2^2, 2^3), so |dP'|, |D'| < 2^14 and |dS'| < 2^15
 // for d <= 128; |c Q'|, |K'| <= 2^14) and fold back exactly into the output
-// scaling.  eq and ek are split so that f = eq + ek = 0 whenever the
+// scaling.  The dQ kernel forms dP from the unscaled dO and V and gives P
+// the same factor 2^-(eo+ev) through its row term, so the dS it rounds to
+// fp16 is the same scaled dS' with the same bound.  eq and ek are split so that f = eq + ek = 0 whenever the
 // geometric mean of max |c Q| and max |K| lies in [2^-4, 2^13]: then the
 // score accumulator, started at -shift, is exactly the exponent of P, and
 // the dP accumulator, started at -D, is exactly dP - D, so P costs one
@@ -253,9 +255,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
   }
 }
 
-// c Q * 2^-eq, K * 2^-ek and dO * 2^-eo as fp16; -shift * 2^-f and -D * 2^-(eo+ev)
-// per row (the initial values of the dK/dV kernel's score and dP
-// accumulators).  Workgroup (b, h) = blockIdx.x / rbph, `iters` blocks of
+// c Q * 2^-eq, K * 2^-ek and dO * 2^-eo as fp16; -(shift + rexp) * 2^-f and
+// -D * 2^-(eo+ev) per row (the initial values of the dK/dV kernel's score and
+// dP accumulators; rexp = 0 without dropout).  Workgroup (b, h) =
+// blockIdx.x / rbph, `iters` blocks of
 // RPB rows from row (blockIdx.x % rbph) * iters * RPB.  Every wave reduces
 // the head's nchunk partial maxima from the D pass itself (iters > 1 on
 // large grids spreads that over more rows); the head's first workgroup
@@ -268,7 +271,8 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, con
                                                           uint32_t* maxes, float c,
                                                           uint16_t* q16, uint16_t* k16,
                                                           uint16_t* do16, float* nDs, float* nsh,
-                                                          int N, int BH, int rbph, int iters) {
+                                                          int N, int BH, int rbph, int iters,
+                                                          int rexp) {
   constexpr int TPR = D / 8;       // threads per row, 16 bytes each
   constexpr int RPB = 256 / TPR;   // rows per workgroup (d = 96: 21, 4 threads idle)
   const int bh = (int)(blockIdx.x / (unsigned)rbph), rb = (int)(blockIdx.x % (unsigned)rbph);
@@ -315,7 +319,9 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, con
     *reinterpret_cast<u32x4*>(k16 + row * D + col) = rk;
     if (col == 0) {
       nDs[row] = -ldexpf(Dbuf[row], -(sc.eo + sc.ev));
-      nsh[row] = sc.exact ? -shift[row] / sc.m : -ldexpf(shift[row], -sc.f);
+      // with dropout the exponent also carries -rexp: P 2^-rexp (see Dropout)
+      const float sh = shift[row] + (float)rexp;
+      nsh[row] = sc.exact ? -sh / sc.m : -ldexpf(sh, -sc.f);
     }
   }
 }
@@ -634,9 +640,11 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
   }
 
   // store dK = scale/c 2^(eq+eo+ev) dK'^T^T (scale/c = ln 2; an exact head's
-  // Q copy carries no c: scale) and dV = 2^eo dV' (4 consecutive d per store)
+  // Q copy carries no c: scale) and dV = 2^eo dV' (4 consecutive d per store);
+  // with dropout both also undo the 2^-rexp that P carried
   if (key < N) {
-    const int ekk = sc.eq + sc.eo + sc.ev;
+    const int rx = DROP ? p.drop.rexp : 0;
+    const int ekk = sc.eq + sc.eo + sc.ev + rx;
     const float kmul = sc.exact ? p.scale : kLn2;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -647,7 +655,7 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           k4[j] = ldexpf(dk[db][4 * i + j] * kmul, ekk);
-          v4[j] = ldexpf(dv[db][4 * i + j], sc.eo);
+          v4[j] = ldexpf(dv[db][4 * i + j], sc.eo + rx);
         }
         *reinterpret_cast<u32x2*>(p.dk + off) = pack4<T>(k4);
         *reinterpret_cast<u32x2*>(p.dv + off) = pack4<T>(v4);
@@ -700,6 +708,16 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
   const int L = valid_keys(p.key_len, b, N);
   const int q0 = qt * kBR, qw = q0 + wave * 32, query = qw + l32;
   const Scales sc = bwd_scales<D>(p.maxes, p.BH, bh, p.c);
+  // dS is rounded to fp16 for dQ = dS K.  dP and D here are unscaled (raw
+  // dO against raw V), so P carries the power of two 2^kq, kq = -(eo + ev),
+  // that the dK/dV kernel's dS gets from its scaled dO and V copies: then
+  // |dS'| = |P 2^kq (dP - D)| <= 2 d max|dO'| max|V'| < 2^15 for d <= 128,
+  // whatever the magnitudes of dO and V, and entries of ordinary size stay
+  // clear of fp16's subnormal range.  kq enters the exponent through the
+  // row term (no instruction per score) and is undone exactly in the
+  // epilogue.  With dropout P also carries 2^-rexp, from the row term the
+  // convert pass wrote.
+  const int kq = -(sc.eo + sc.ev);
   // D of this lane's query (dropout: subtracted after the mask)
   const float dq_D = DROP && query < N ? p.Dbuf[(size_t)bh * N + query] : 0.f;
 
@@ -720,7 +738,10 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
   // fp32 accumulator starts from them exactly
   f32x16 s_init, dp_init;
   {
-    const float ns = qok ? p.nsh[(size_t)bh * N + query] : neg_inf();
+    // the exponent is m (nsh + S'') when the accumulator is rescaled by m
+    // (m = 2^f, or c 2^f in exact mode), else nsh + S''
+    const float kqm = sc.mul ? (float)kq / sc.m : (float)kq;
+    const float ns = qok ? p.nsh[(size_t)bh * N + query] + kqm : neg_inf();
     const float nd = qok && !DROP ? -p.Dbuf[(size_t)bh * N + query] : 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -874,14 +895,15 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
     walk(nkt, [](int t) { return t * kBC; });
   }
 
-  if (qok) {  // dQ = scale 2^ek (dS K')
+  if (qok) {  // dQ = scale 2^(ek - kq + rexp) (dS' K')
+    const int eqo = sc.ek - kq + (DROP ? p.drop.rexp : 0);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 q4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) q4[j] = ldexpf(acc[db][4 * i + j] * p.scale, sc.ek);
+        for (int j = 0; j < 4; ++j) q4[j] = ldexpf(acc[db][4 * i + j] * p.scale, eqo);
         *reinterpret_cast<u32x2*>(p.dq + base + (size_t)query * D + db * 32 + 8 * i + 4 * h) =
             pack4<T>(q4);
       }
@@ -944,7 +966,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_fused_kernel(BwdPara
   template __global__ void bwd_convert_kernel<T, D>(                               \
       const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*,   \
       const uint32_t*, int, uint32_t*, float,                                        \
-      uint16_t*, uint16_t*, uint16_t*, float*, float*, int, int, int, int);
+      uint16_t*, uint16_t*, uint16_t*, float*, float*, int, int, int, int, int);
 FA_BWD_INSTANTIATE(__bf16, 32)
 FA_BWD_INSTANTIATE(__bf16, 64)
 FA_BWD_INSTANTIATE(__bf16, 96)
@@ -1001,7 +1023,7 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
     hipLaunchKernelGGL((bwd_convert_kernel<T, D>), dim3((unsigned)((int64_t)BH * rbph)),
                        dim3(256), 0, a.stream, q, static_cast<const uint16_t*>(a.k), dO, Dbuf,
                        shift, part, nchunk, maxes, c, q16, k16, do16, nDs, nsh, a.N, BH, rbph,
-                       citers);
+                       citers, a.drop.on ? a.drop.rexp : 0);
     e = hipGetLastError();
     if (e != hipSuccess || stage == 1) return e;
   }
@@ -1033,7 +1055,7 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   p.period = (FA_BWD_SNAKE && CAUSAL) ? snake_period(p.BH) : 0;
   p.drop = a.drop;
 
-  if (stage == 0) {
+  if (stage == 0 || stage == 4) {
     p.ntiles = (a.N + kBKV - 1) / kBKV;
     hipLaunchKernelGGL((bwd_fused_kernel<T, D, CAUSAL, SPARSE, DROP>),
                        dim3(2 * p.ntiles * p.BH), dim3(256), 0, a.stream, p);

@@ -291,13 +291,13 @@ hipError_t run(const BwdArgs& a, int stage) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stage == 0 || stage == 2) {
+  if (stage == 0 || stage == 2 || stage == 4) {
     hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(p.ntiles * p.BH), dim3(256), 0, a.stream,
                        p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stage == 0 || stage == 3) {
+  if (stage == 0 || stage == 3 || stage == 4) {
     hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(p.ntiles * p.BH), dim3(256), 0, a.stream,
                        p);
     e = hipGetLastError();

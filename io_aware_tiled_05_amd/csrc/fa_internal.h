@@ -20,6 +20,10 @@ struct Dropout {
   int on = 0;
   uint32_t thresh = 0;
   float rinv = 1.f;
+  // ceil(log2(rinv)): the 16-bit backward takes 2^-rexp into P, so that
+  // P M rinv 2^-rexp <= 1 and dS keeps the same fp16 range bound as
+  // without dropout (undone exactly in the gradients' fp32 epilogues)
+  int rexp = 0;
   uint32_t k0 = 0, k1 = 0, offset = 0;
 };
 
@@ -147,7 +151,8 @@ inline DecodeSplit decode_split(int64_t B, int64_t H, int64_t Nq, int64_t Nk, in
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_fwd(const FwdArgs& a);
 // stage 0: the whole backward (16-bit: the D pass, then one launch that runs
-// the dK/dV and dQ workgroups together); 1: D only; 2: dK/dV only; 3: dQ only
+// the dK/dV and dQ workgroups together); 1: D only; 2: dK/dV only; 3: dQ only;
+// 4: dK/dV and dQ as stage 0 runs them (16-bit: the one launch)
 hipError_t launch_bwd(const BwdArgs& a, int stage);
 // fp32 inputs (dense, causal, key padding; no block mask); same stages
 hipError_t launch_bwd_f32(const BwdArgs& a, int stage);

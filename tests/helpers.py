@@ -13,15 +13,20 @@ class Tol(float):
 
 TOL = {"f32": Tol(1e-5, "f32"), "f16": Tol(1e-2, "f16"), "bf16": Tol(2e-2, "bf16")}
 
-# stored significand bits (without the hidden bit) of each output dtype
+# stored significand bits (without the hidden bit) and smallest normal
+# exponent of each output dtype
 _MANT = {"f32": 23, "f16": 10, "bf16": 7}
+_EMIN = {"f32": -126, "f16": -14, "bf16": -126}
 
 
 def half_spacing(ref, dtype):
     """Half the distance between neighbouring ``dtype`` values at |ref|: the
-    error that storing the exact result in that dtype can cost."""
+    error that storing the exact result in that dtype can cost.  Below the
+    dtype's normal range the spacing stays that of its subnormals (fp16:
+    2^-24 under 2^-14)."""
     a = np.maximum(np.abs(np.asarray(ref, dtype=np.float64)), np.finfo(np.float64).tiny)
-    return np.ldexp(1.0, np.floor(np.log2(a)).astype(np.int64) - _MANT[dtype] - 1)
+    e = np.maximum(np.floor(np.log2(a)).astype(np.int64), _EMIN[dtype])
+    return np.ldexp(1.0, e - _MANT[dtype] - 1)
 
 
 def allowance(ref, tol):

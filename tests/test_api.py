@@ -174,7 +174,7 @@ def stage(lib, st, **kw):
 
 
 @pytest.mark.parametrize("st,kw,status", [
-    (0, {}, -1), (4, {}, -1), (-1, {}, -1),
+    (0, {}, -1), (5, {}, -1), (-1, {}, -1), (4, dict(d=80), -2), (4, dict(ws=None), -1),
     (1, dict(ws=None), -1), (2, dict(d=80), -2), (3, dict(dtype=F32, bm=P), -2),
     (2, dict(bm=P, causal=1), -1), (2, dict(bm=P, key_len=P), -1), (3, dict(bm=P, bs=64), -2),
     (1, dict(ws_bytes=8), -1),

@@ -1,7 +1,8 @@
 """The backward as one call (fa_bwd: the D pass, then one launch that runs the
-dK/dV and dQ workgroups together) and as its three stages launched one at a
-time (fa_bwd_stage) must give the same gradients bit for bit: every output
-element is computed by the same arithmetic in both.  The one-call form is
+dK/dV and dQ workgroups together), as its three stages launched one at a
+time, and as the D stage followed by the one-launch gradient stage
+(fa_bwd_stage 1, 2, 3 and 1, 4) must give the same gradients bit for bit:
+every output element is computed by the same arithmetic in all three.  The one-call form is
 checked against the fp64 oracle by test_parity_bwd.py; one case here is
 checked against it too, through the staged form.
 """
@@ -42,7 +43,13 @@ def both(fa, x, dtype, causal=False, key_len=None, block_mask=None):
     for st in (fa.FA_BWD_STAGE_D, fa.FA_BWD_STAGE_DKDV, fa.FA_BWD_STAGE_DQ):
         fa.fa_bwd_stage(st, q, k, v, o, lse, dO, dq, dk, dv, ws, scale=s, causal=causal,
                         key_len=kl, block_mask=bm)
+    g4 = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    for st in (fa.FA_BWD_STAGE_D, fa.FA_BWD_STAGE_GRADS):
+        fa.fa_bwd_stage(st, q, k, v, o, lse, dO, *g4, ws, scale=s, causal=causal, key_len=kl,
+                        block_mask=bm)
     torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), one, g4):
+        assert bool((a == b).all()), f"{name} differs between fa_bwd and stages 1, 4"
     return one, (dq, dk, dv)
 
 

@@ -19,13 +19,14 @@ held to tol * max(factor, |reference|): the scaled gate, or the gate
 relative to the element's own size where that is larger (the relative
 reading the absolute gate falls back to once values exceed what a 16-bit
 store can hold to within it).  One exception, bf16 with large logits: the
-backward forms D = sum dO O from O as stored in bf16, and with nearly
-one-hot rows a dominant key collects that rounding from every row it
-dominates while its true gradient nearly cancels; measured up to 1.14 times
-the scaled gate at q, k x 2 .. 5 (against 0.4 at x 1), so that case is held
-to twice it.  The fp16 inputs, which run the same backward kernels after the
-same conversion but store O with 3 more bits, are held to the plain scaled
-gate there.  (Far beyond, at q, k x 30 with
+backward forms D = sum dO O from O as the forward stored it, in bf16, and
+with nearly one-hot rows a dominant key collects that rounding from every
+row it dominates while its true gradient nearly cancels.  Measured: dK up to
+1.14 times the scaled gate at q, k x 5 (dQ 0.80, against 0.4 at x 1), so
+that case is held to 1.25 times it (the measured bound and a 10 % margin).
+The fp16 inputs, which run the same backward kernels after the same
+conversion but store O with 3 more bits, are held to the plain scaled gate
+there.  (Far beyond, at q, k x 30 with
 logits near 3000, fp32 itself bounds the recomputed P to about 0.3 %; the
 exact-scores mode keeps dQ and dK within 0.7 % of their size there, against
 40 % without it.)
@@ -67,7 +68,7 @@ def test_extreme_magnitudes(fa, dtype, causal, case):
     ro, rl = attention_fwd(x["q"], x["k"], x["v"], x["scale"], causal=causal)
     rq, rk, rv = attention_bwd(x["q"], x["k"], x["v"], x["dO"], x["scale"], causal=causal)
     f = {n: CASES[case].get(n, 1.0) for n in ("q", "k", "v", "dO")}
-    t = float(TOL[dtype]) * (2.0 if (case, dtype) == ("large_qk", "bf16") else 1.0)
+    t = float(TOL[dtype]) * (1.25 if (case, dtype) == ("large_qk", "bf16") else 1.0)
     scaled("o", to_np(o), ro, float(TOL[dtype]), f["v"])
     assert_close("lse", to_np(lse), rl, TOL[dtype])
     scaled("dq", to_np(dq), rq, t, f["dO"] * f["v"] * f["k"])
