@@ -3,8 +3,16 @@
 Thin wrappers over the C ABI of ``libfa.so`` (include/fa.h) with the same
 names.  They only marshal arguments: check shapes, dtypes and devices of
 torch tensors, allocate outputs with torch, and pass raw device pointers plus
-the current HIP stream.  Every step of the computation runs in the HIP
-kernels; there is no CPU or PyTorch fallback.
+the HIP stream.  Every step of the computation runs in the HIP kernels; there
+is no CPU or PyTorch fallback.
+
+Every buffer a caller passes (outputs, lse, workspace, key lengths, block
+masks) is checked for shape, dtype, device and layout before its pointer
+reaches the library, since the kernels write through it without bounds.
+When ``stream`` is not the current stream, tensors that the binding
+allocates are marked as used on ``stream`` (``record_stream``), so torch's
+caching allocator does not hand their memory to other work while the
+kernels still run.
 """
 
 from __future__ import annotations
@@ -13,12 +21,12 @@ import math
 
 from ._lib import (FA_BF16, FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ,  # noqa: F401
                    FA_BWD_STAGE_GRADS,  # noqa: F401
-                   FA_ERR_HIP, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_F16,  # noqa: F401
-                   FA_F32, FA_OK, FaError, check, load)
+                   FA_ERR_HIP, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_F16, FA_F32,  # noqa: F401
+                   FA_OK, FaError, check, load)
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_blocksparse", "fa_bwd_blocksparse", "fa_bwd_stage",
-           "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd_dropout",
-           "fa_bwd_dropout", "FaError", "load"]
+__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_blocksparse", "fa_bwd_blocksparse",
+           "fa_bwd_stage", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size",
+           "fa_fwd_dropout", "fa_bwd_dropout", "FaError", "load"]
 
 
 def _torch():
@@ -35,16 +43,33 @@ def _dtype_code(t):
 
 
 def _check_qkv(*ts):
+    """Tensors of q's shape, dtype and device, contiguous [B, H, N, d]."""
     q = ts[0]
     if q.dim() != 4:
         raise ValueError("expected [B, H, N, d] tensors")
     for t in ts:
         if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("q, k, v (and o, dO) must share shape and dtype")
+            raise ValueError("q, k, v, o, dO and the gradients must share shape and dtype")
         if not t.is_cuda or t.device != q.device:
             raise ValueError("tensors must be on the same GPU")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous [B, H, N, d]")
+
+
+def _check_lse(lse, q, rows=None):
+    """lse: contiguous float32 [B, H, rows] (rows = N) on q's device."""
+    torch = _torch()
+    B, H, N = q.shape[0], q.shape[1], q.shape[2] if rows is None else rows
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_cuda
+            or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 tensor [{B}, {H}, {N}] on q's GPU")
+
+
+def _check_workspace(ws, q, need):
+    if not ws.is_cuda or ws.device != q.device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's GPU")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes; {need} needed")
 
 
 def _ptr(t):
@@ -56,6 +81,17 @@ def _stream(stream, q):
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     return stream.cuda_stream
+
+
+def _keep(stream, q, *ts):
+    """Mark tensors the binding allocated (or copied) as in use on
+    ``stream`` when it is not q's current stream."""
+    torch = _torch()
+    if stream is None or stream == torch.cuda.current_stream(q.device):
+        return
+    for t in ts:
+        if t is not None:
+            t.record_stream(stream)
 
 
 def _call(q, name, *args):
@@ -70,28 +106,54 @@ def _key_len(key_len, q):
     torch = _torch()
     if key_len is None:
         return None
-    if key_len.dtype != torch.int32 or key_len.device != q.device or key_len.numel() != q.shape[0]:
+    if (key_len.dtype != torch.int32 or not key_len.is_cuda or key_len.device != q.device
+            or key_len.numel() != q.shape[0]):
         raise ValueError("key_len must be an int32 tensor [B] on the same GPU")
     return key_len.contiguous()
+
+
+def _block_mask(block_mask, q, block_size):
+    torch = _torch()
+    if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda
+            or block_mask.device != q.device or block_mask.dim() != 2):
+        raise ValueError("block_mask must be a uint8 [nb, nb] tensor on the same GPU")
+    nb = (q.shape[2] + block_size - 1) // block_size
+    if tuple(block_mask.shape) != (nb, nb):
+        raise ValueError(f"block_mask must be [{nb}, {nb}]")
+    return block_mask.contiguous()
 
 
 def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
+def _fwd_outputs(q, out, lse):
+    """(o, lse, allocated): the caller's buffers checked, or new ones."""
+    torch = _torch()
+    B, H, N, _ = q.shape
+    made = []
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+        made.append(out)
+    _check_qkv(q, out)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        made.append(lse)
+    _check_lse(lse, q)
+    return out, lse, made
+
+
 def fa_fwd(q, k, v, scale=None, causal=False, key_len=None, out=None, lse=None,
            stream=None):
     """O, lse = softmax(q k^T * scale + mask) v; see include/fa.h (fa_fwd)."""
-    torch = _torch()
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     kl = _key_len(key_len, q)
-    o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check_qkv(q, o)
+    o, lse, made = _fwd_outputs(q, out, lse)
     st = _call(q, "fa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                _scale(scale, d), int(bool(causal)), _ptr(kl), _dtype_code(q), _stream(stream, q))
     check("fa_fwd", st)
+    _keep(stream, q, kl, *made)
     return o, lse
 
 
@@ -100,54 +162,53 @@ def fa_bwd_workspace_size(B, H, N, d):
 
 
 def _bwd_outputs(q, dq, dk, dv, workspace):
+    """(dq, dk, dv, workspace, allocated): the caller's buffers checked, or
+    new ones."""
     torch = _torch()
     B, H, N, d = q.shape
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    made = []
+    grads = []
+    for g in (dq, dk, dv):
+        if g is None:
+            g = torch.empty_like(q, memory_format=torch.contiguous_format)
+            made.append(g)
+        grads.append(g)
+    _check_qkv(q, *grads)
     need = fa_bwd_workspace_size(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
-    return dq, dk, dv, workspace
+        made.append(workspace)
+    _check_workspace(workspace, q, need)
+    return (*grads, workspace, made)
 
 
 def fa_bwd(q, k, v, o, lse, dO, scale=None, causal=False, key_len=None, dq=None, dk=None,
            dv=None, workspace=None, stream=None):
     """dq, dk, dv of sum(dO * O); see include/fa.h (fa_bwd)."""
     _check_qkv(q, k, v, o, dO)
+    _check_lse(lse, q)
     B, H, N, d = q.shape
     kl = _key_len(key_len, q)
-    dq, dk, dv, ws = _bwd_outputs(q, dq, dk, dv, workspace)
-    _check_qkv(q, dq, dk, dv)
+    dq, dk, dv, ws, made = _bwd_outputs(q, dq, dk, dv, workspace)
     st = _call(q, "fa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
                _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(kl),
                _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(q), _stream(stream, q))
     check("fa_bwd", st)
+    _keep(stream, q, kl, *made)
     return dq, dk, dv
-
-
-def _block_mask(block_mask, q):
-    torch = _torch()
-    if block_mask.dtype != torch.uint8 or block_mask.device != q.device or block_mask.dim() != 2:
-        raise ValueError("block_mask must be a uint8 [nb, nb] tensor on the same GPU")
-    return block_mask.contiguous()
 
 
 def fa_fwd_blocksparse(q, k, v, block_mask, block_size=128, scale=None, out=None, lse=None,
                        stream=None):
     """Block-sparse forward; see include/fa.h (fa_fwd_blocksparse)."""
-    torch = _torch()
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
-    bm = _block_mask(block_mask, q)
-    nb = (N + block_size - 1) // block_size
-    if bm.shape != (nb, nb):
-        raise ValueError(f"block_mask must be [{nb}, {nb}]")
-    o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    bm = _block_mask(block_mask, q, block_size)
+    o, lse, made = _fwd_outputs(q, out, lse)
     st = _call(q, "fa_fwd_blocksparse", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                _scale(scale, d), _ptr(bm), block_size, _dtype_code(q), _stream(stream, q))
     check("fa_fwd_blocksparse", st)
+    _keep(stream, q, bm, *made)
     return o, lse
 
 
@@ -155,16 +216,15 @@ def fa_bwd_blocksparse(q, k, v, o, lse, dO, block_mask, block_size=128, scale=No
                        dk=None, dv=None, workspace=None, stream=None):
     """Block-sparse backward; see include/fa.h (fa_bwd_blocksparse)."""
     _check_qkv(q, k, v, o, dO)
+    _check_lse(lse, q)
     B, H, N, d = q.shape
-    bm = _block_mask(block_mask, q)
-    nb = (N + block_size - 1) // block_size
-    if bm.shape != (nb, nb):
-        raise ValueError(f"block_mask must be [{nb}, {nb}]")
-    dq, dk, dv, ws = _bwd_outputs(q, dq, dk, dv, workspace)
+    bm = _block_mask(block_mask, q, block_size)
+    dq, dk, dv, ws, made = _bwd_outputs(q, dq, dk, dv, workspace)
     st = _call(q, "fa_bwd_blocksparse", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
                _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d), _ptr(bm), block_size,
                _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(q), _stream(stream, q))
     check("fa_bwd_blocksparse", st)
+    _keep(stream, q, bm, *made)
     return dq, dk, dv
 
 
@@ -173,14 +233,17 @@ def fa_bwd_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, workspace, scale=None, 
     """One stage of the backward (FA_BWD_STAGE_D, _DKDV, _DQ or _GRADS); outputs and
     workspace are caller-allocated; see include/fa.h (fa_bwd_stage)."""
     _check_qkv(q, k, v, o, dO, dq, dk, dv)
+    _check_lse(lse, q)
     B, H, N, d = q.shape
+    _check_workspace(workspace, q, fa_bwd_workspace_size(B, H, N, d))
     kl = _key_len(key_len, q)
-    bm = None if block_mask is None else _block_mask(block_mask, q)
+    bm = None if block_mask is None else _block_mask(block_mask, q, block_size)
     st = _call(q, "fa_bwd_stage", int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d),
                int(bool(causal)), _ptr(kl), _ptr(bm), block_size, _ptr(workspace),
                workspace.numel() * workspace.element_size(), _dtype_code(q), _stream(stream, q))
     check("fa_bwd_stage", st)
+    _keep(stream, q, kl, bm)
 
 
 def fa_decode_workspace_size(B, H, Nq, Nk, d):
@@ -203,15 +266,17 @@ def fa_decode(q, k, v, scale=None, key_len=None, out=None, lse=None, workspace=N
     if k.shape != (B, H, Nk, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
     kl = _key_len(key_len, q)
-    o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o, lse, made = _fwd_outputs(q, out, lse)
     need = fa_decode_workspace_size(B, H, Nq, Nk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+        made.append(workspace)
+    _check_workspace(workspace, q, need)
     st = _call(q, "fa_decode", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
                _scale(scale, d), _ptr(kl), _ptr(workspace),
                workspace.numel() * workspace.element_size(), _dtype_code(q), _stream(stream, q))
     check("fa_decode", st)
+    _keep(stream, q, kl, *made)
     return o, lse
 
 
@@ -226,18 +291,16 @@ def fa_fwd_dropout(q, k, v, dropout_p, seed, offset=0, scale=None, causal=False,
                    out=None, lse=None, stream=None):
     """fa_fwd with dropout on the probabilities; see include/fa.h
     (fa_fwd_dropout).  Returns (O, lse)."""
-    torch = _torch()
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     kl = _key_len(key_len, q)
     sd, off = _seed(seed, offset)
-    o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check_qkv(q, o)
+    o, lse, made = _fwd_outputs(q, out, lse)
     st = _call(q, "fa_fwd_dropout", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                _scale(scale, d), int(bool(causal)), _ptr(kl), float(dropout_p), sd, off,
                _dtype_code(q), _stream(stream, q))
     check("fa_fwd_dropout", st)
+    _keep(stream, q, kl, *made)
     return o, lse
 
 
@@ -246,14 +309,15 @@ def fa_bwd_dropout(q, k, v, o, lse, dO, dropout_p, seed, offset=0, scale=None, c
     """Backward of fa_fwd_dropout (same dropout_p, seed, offset); see
     include/fa.h (fa_bwd_dropout).  Returns (dq, dk, dv)."""
     _check_qkv(q, k, v, o, dO)
+    _check_lse(lse, q)
     B, H, N, d = q.shape
     kl = _key_len(key_len, q)
     sd, off = _seed(seed, offset)
-    dq, dk, dv, ws = _bwd_outputs(q, dq, dk, dv, workspace)
-    _check_qkv(q, dq, dk, dv)
+    dq, dk, dv, ws, made = _bwd_outputs(q, dq, dk, dv, workspace)
     st = _call(q, "fa_bwd_dropout", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
                _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)),
                _ptr(kl), float(dropout_p), sd, off, _ptr(ws), ws.numel() * ws.element_size(),
                _dtype_code(q), _stream(stream, q))
     check("fa_bwd_dropout", st)
+    _keep(stream, q, kl, *made)
     return dq, dk, dv
