@@ -37,7 +37,9 @@
  *                       block-sparse);
  *   FA_ERR_HIP          a kernel launch failed (hipGetLastError).  Faults
  *                       during kernel execution surface at the caller's next
- *                       synchronisation, as for any asynchronous launch.
+ *                       synchronisation, as for any asynchronous launch;
+ *   FA_ERR_TOO_LARGE    (fa_bwd_noalloc only) the problem needs more
+ *                       workspace than the library's fixed array holds.
  * Masks.  Combined with AND.  causal: key j visible to query i iff j <= i.
  *   key_len (nullable): key j of batch element b visible iff j < key_len[b];
  *   key_len[b] outside [0, N] is clamped to that range.  Rows that see no
@@ -63,7 +65,8 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID = -1,
   FA_ERR_UNSUPPORTED = -2,
-  FA_ERR_HIP = -3
+  FA_ERR_HIP = -3,
+  FA_ERR_TOO_LARGE = -4
 } fa_status;
 
 /* Forward.  [ODP "The key idea"]: the queries, keys and values are split
@@ -227,6 +230,34 @@ size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d);
 int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
               int Nq, int Nk, int d, float scale, const int32_t* key_len, void* workspace,
               size_t workspace_bytes, int dtype, void* stream);
+
+/* Size in bytes of the device array that fa_bwd_noalloc uses as its
+ * workspace (128 MiB; one copy per GPU the library runs on). */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* fa_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * It computes exactly what fa_bwd computes (the same kernels and launch
+ * sequence), but its workspace is a fixed array of FA_NOALLOC_SCRATCH_BYTES
+ * inside the library instead of a caller-provided buffer; it calls no
+ * allocation routine.  The caller still passes and owns every input and
+ * output.  Dense, causal or key-padded (no block mask, no dropout); dtype
+ * FA_F32, FA_F16 or FA_BF16.
+ *   Limit: fa_bwd_workspace_size(B, H, N, d) <= FA_NOALLOC_SCRATCH_BYTES,
+ *   else FA_ERR_TOO_LARGE (for example B=1, H=16, N=16384, d=64 needs
+ *   100 MiB and fits; d=128 at that size needs 196 MiB and does not).
+ *   Sharing: every call on one GPU uses that GPU's one array, so calls
+ *   that overlap in time on one GPU (different streams or host threads
+ *   without ordering between them) race and give wrong results; calls
+ *   ordered on one stream are fine.  The array keeps the last call's
+ *   contents; nothing in it needs clearing between calls.
+ *   Errors: as fa_bwd, checked before any HIP call, plus FA_ERR_TOO_LARGE;
+ *   FA_ERR_HIP if the array's device address cannot be obtained (looked up
+ *   once per device, on the first call with that device current). */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const int32_t* key_len, int dtype, void* stream);
 
 /* Static description of a status code ("ok", "invalid argument", ...). */
 const char* fa_status_string(int status);

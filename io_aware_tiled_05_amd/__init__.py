@@ -21,10 +21,11 @@ import math
 
 from ._lib import (FA_BF16, FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ,  # noqa: F401
                    FA_BWD_STAGE_GRADS,  # noqa: F401
-                   FA_ERR_HIP, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_F16, FA_F32,  # noqa: F401
-                   FA_OK, FaError, check, load)
+                   FA_ERR_HIP, FA_ERR_INVALID, FA_ERR_TOO_LARGE, FA_ERR_UNSUPPORTED,  # noqa: F401
+                   FA_F16, FA_F32, FA_NOALLOC_SCRATCH_BYTES, FA_OK, FaError, check,  # noqa: F401
+                   load)
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_fwd_blocksparse", "fa_bwd_blocksparse",
+__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_fwd_blocksparse", "fa_bwd_blocksparse",
            "fa_bwd_stage", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size",
            "fa_fwd_dropout", "fa_bwd_dropout", "FaError", "load"]
 
@@ -195,6 +196,25 @@ def fa_bwd(q, k, v, o, lse, dO, scale=None, causal=False, key_len=None, dq=None,
                _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(q), _stream(stream, q))
     check("fa_bwd", st)
     _keep(stream, q, kl, *made)
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, scale=None, causal=False, key_len=None,
+                   stream=None):
+    """fa_bwd with the library's fixed workspace array; dq, dk, dv are the
+    caller's (contiguous [B, H, N, d], q's dtype and device), and nothing is
+    allocated on the way to the C call (key_len must be contiguous); see
+    include/fa.h (fa_bwd_noalloc)."""
+    _check_qkv(q, k, v, o, dO, dq, dk, dv)
+    _check_lse(lse, q)
+    B, H, N, d = q.shape
+    if key_len is not None and not key_len.is_contiguous():
+        raise ValueError("key_len must be contiguous (fa_bwd_noalloc makes no copies)")
+    kl = _key_len(key_len, q)
+    st = _call(q, "fa_bwd_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)),
+               _ptr(kl), _dtype_code(q), _stream(stream, q))
+    check("fa_bwd_noalloc", st)
     return dq, dk, dv
 
 

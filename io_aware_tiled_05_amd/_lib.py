@@ -12,7 +12,8 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
-FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, -1, -2, -3, -4
+FA_NOALLOC_SCRATCH_BYTES = 128 << 20
 FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ, FA_BWD_STAGE_GRADS = 1, 2, 3, 4
 
 # (name, restype, argtypes) for every function in include/fa.h
@@ -33,6 +34,8 @@ SIGNATURES = {
                             C.c_uint64, C.c_uint32, _P, _SZ, _I, _P]),
     "fa_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _I, _P]),
+    "fa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I,
+                            _P]),
     "fa_status_string": (C.c_char_p, [_I]),
 }
 

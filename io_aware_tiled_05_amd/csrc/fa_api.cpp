@@ -80,18 +80,11 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
                float scale, int causal, const int32_t* key_len, const uint8_t* block_mask,
                void* workspace, size_t workspace_bytes, int dtype, void* stream,
                int stage, const fa::Dropout& drop = fa::Dropout{}) {
-  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
-    return FA_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
-    return FA_ERR_INVALID;
-  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
-  int st = check_dtype(dtype);
-  if (st == FA_OK) st = check_scale(scale);
-  if (st == FA_OK) st = check_sizes(B, H, N, d);
+  if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID;
+  const int st = fa::bwd_check(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal,
+                               block_mask != nullptr, dtype, drop.on != 0);
   if (st != FA_OK) return st;
   if (workspace_bytes < fa_bwd_workspace_size(B, H, N, d)) return FA_ERR_INVALID;
-  if (dtype == FA_F32 && (block_mask || drop.on)) return FA_ERR_UNSUPPORTED;
   fa::BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
                 block_mask, workspace, dtype,
                 static_cast<hipStream_t>(stream), drop};
@@ -101,6 +94,23 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
 }  // namespace
 
 namespace fa {
+
+int bwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dO, const void* dq, const void* dk, const void* dv, int B, int H,
+              int N, int d, float scale, int causal, bool block_sparse, int dtype,
+              bool dropout) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  int st = check_dtype(dtype);
+  if (st == FA_OK) st = check_scale(scale);
+  if (st == FA_OK) st = check_sizes(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32 && (block_sparse || dropout)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
 
 int device_cu_count() {
   // per device id; 0 = not queried yet.  Concurrent callers may both query
@@ -227,6 +237,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_INVALID: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported configuration";
     case FA_ERR_HIP: return "HIP launch error";
+    case FA_ERR_TOO_LARGE:
+      return "problem too large for the library's fixed scratch buffer (fa_bwd_noalloc)";
     default: return "unknown status";
   }
 }

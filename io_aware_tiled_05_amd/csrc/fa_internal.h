@@ -102,6 +102,13 @@ inline BwdWorkspace bwd_workspace_layout(int64_t B, int64_t H, int64_t N, int64_
   return w;
 }
 
+// The checks of fa_bwd's arguments (everything but the workspace), made
+// before any HIP call; FA_OK or the status to return.
+int bwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dO, const void* dq, const void* dk, const void* dv, int B, int H,
+              int N, int d, float scale, int causal, bool block_sparse, int dtype,
+              bool dropout);
+
 // Compute units of the current device (0 if the query fails); cached.
 int device_cu_count();
 

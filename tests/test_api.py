@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_dropout", "fa_bwd_stage", "fa_bwd_workspace_size",
+        "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_dropout", "fa_bwd_noalloc", "fa_bwd_stage",
+        "fa_bwd_workspace_size",
         "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_blocksparse",
         "fa_fwd_dropout", "fa_status_string"])
 
@@ -63,6 +64,7 @@ def test_status_strings(lib):
     assert lib.fa_status_string(-1) == b"invalid argument"
     assert lib.fa_status_string(-2) == b"unsupported configuration"
     assert lib.fa_status_string(-3) == b"HIP launch error"
+    assert b"fixed scratch buffer" in lib.fa_status_string(-4)
     assert lib.fa_status_string(7) == b"unknown status"
 
 
@@ -137,6 +139,38 @@ def bwd(lib, blocksparse=False, **kw):
 ])
 def test_bwd_validation(lib, kw, status):
     assert bwd(lib, **kw) == status
+
+
+def noalloc(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, dO=P, dq=P, dk=P, dv=P, B=2, H=2, N=256, d=64,
+             scale=0.125, causal=0, key_len=None, dtype=BF16)
+    a.update(kw)
+    return lib.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"], a["dq"],
+                              a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                              a["causal"], a["key_len"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dO=None), -1), (dict(dv=None), -1), (dict(lse=None), -1), (dict(dq=P + 4), -1),
+    (dict(d=80), -2), (dict(scale=-1.0), -1), (dict(N=0), -1), (dict(causal=3), -1),
+    (dict(dtype=9), -1),
+    # fa_bwd_workspace_size(1, 16, 16384, 128) = 196 MiB > the 128 MiB array
+    (dict(B=1, H=16, N=16384, d=128), -4),
+    (dict(B=4, H=16, N=16384, d=64), -4),
+])
+def test_bwd_noalloc_validation(lib, kw, status):
+    # every case is rejected before any HIP call
+    assert noalloc(lib, **kw) == status
+
+
+def test_noalloc_scratch_limit_matches_header(lib):
+    from io_aware_tiled_05_amd import _lib
+    src = open(HEADER).read()
+    assert "#define FA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in src
+    assert _lib.FA_NOALLOC_SCRATCH_BYTES == 128 << 20
+    # the bench workload's backward fits it, twice its size does not
+    assert lib.fa_bwd_workspace_size(1, 16, 16384, 64) <= 128 << 20
+    assert lib.fa_bwd_workspace_size(2, 16, 16384, 64) > 128 << 20
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -120,6 +120,8 @@ def test_backward_rejects_bad_lse(bad):
     with pytest.raises(ValueError, match="lse"):
         fa.fa_bwd(q, k, v, o, BAD_LSE[bad], dO, dq=g[0], dk=g[1], dv=g[2], workspace=ws)
     with pytest.raises(ValueError, match="lse"):
+        fa.fa_bwd_noalloc(q, k, v, o, BAD_LSE[bad], dO, *g)
+    with pytest.raises(ValueError, match="lse"):
         fa.fa_bwd_stage(fa.FA_BWD_STAGE_D, q, k, v, o, BAD_LSE[bad], dO, *g, ws)
 
 
@@ -136,6 +138,8 @@ def test_backward_rejects_bad_gradient_buffers(which, bad):
     with pytest.raises(ValueError):
         fa.fa_bwd_blocksparse(q, k, v, o, lse, dO, T((1, 1), torch.uint8), dq=g[0], dk=g[1],
                               dv=g[2], workspace=ws)
+    with pytest.raises(ValueError):
+        fa.fa_bwd_noalloc(q, k, v, o, lse, dO, *g)
 
 
 def test_backward_rejects_short_workspace():
@@ -175,3 +179,11 @@ def test_block_mask_and_key_len_checked():
         fa.fa_fwd(q, k, v, key_len=T((B + 1,), torch.int32), out=out, lse=lse)
     with pytest.raises(ValueError, match="key_len"):
         fa.fa_fwd(q, k, v, key_len=T((B,), torch.int64), out=out, lse=lse)
+
+
+def test_noalloc_refuses_strided_key_len():
+    q, k, v = qkv()
+    o, dO, lse = T((B, H, N, D)), T((B, H, N, D)), T(**GOOD_LSE)
+    g = [T((B, H, N, D)) for _ in range(3)]
+    with pytest.raises(ValueError, match="key_len"):
+        fa.fa_bwd_noalloc(q, k, v, o, lse, dO, *g, key_len=T((B,), torch.int32, contiguous=False))
