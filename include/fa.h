@@ -69,6 +69,21 @@ typedef enum {
   FA_ERR_TOO_LARGE = -4
 } fa_status;
 
+/* Element strides of one [B][H][N][d] tensor view: element (b, h, i, c)
+ * lies at base + b*batch + h*head + i*row + c (the d index is contiguous).
+ * A packed tensor has row = d, head = N*d, batch = H*N*d; the [B][N][H][d]
+ * layout of most framework code, viewed as [B][H][N][d], has row = H*d,
+ * head = d, batch = N*H*d. */
+typedef struct {
+  int64_t batch, head, row;
+} fa_strides;
+
+/* The strides of every tensor a call touches (fields a call does not use
+ * are ignored); a NULL layout means every tensor is packed. */
+typedef struct {
+  fa_strides q, k, v, o, dO, dq, dk, dv;
+} fa_layout;
+
 /* Forward.  [ODP "The key idea"]: the queries, keys and values are split
  * into blocks that fit on-chip, a running row maximum and running row sum
  * are kept per query, and the partial output is rescaled as each key/value
@@ -206,6 +221,40 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                    int H, int N, int d, float scale, int causal, const int32_t* key_len,
                    float dropout_p, uint64_t seed, uint32_t offset, void* workspace,
                    size_t workspace_bytes, int dtype, void* stream);
+
+/* The forward on tensors of any fa_layout, with every mask and option of
+ * the entry points above in one call: causal and key_len (as fa_fwd),
+ * block_mask and block_size (as fa_fwd_blocksparse; then causal must be 0,
+ * key_len NULL and dropout_p 0), dropout_p, seed and offset (as
+ * fa_fwd_dropout; dropout_p = 0: none).  This is the call for tensors that
+ * are views of a framework's storage, e.g. [B][N][H][d] activations or the
+ * q, k, v slices of a fused projection: the kernels read and write them in
+ * place, with no transposing copy ([DEC "The Passage"]: the kernel behind
+ * scaled_dot_product_attention, whose inputs are such views).
+ *   layout : strides of q, k, v, o in elements (NULL: packed).  Every
+ *            stride must be >= 0 and a multiple of 8 elements (16-bit
+ *            dtypes) or 4 (FA_F32), row strides below 2^24, and o's row
+ *            stride at least d; otherwise FA_ERR_INVALID.  lse is always a
+ *            packed [B][H][N] array.
+ * Everything else as fa_fwd. */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const int32_t* key_len, const uint8_t* block_mask, int block_size,
+                   float dropout_p, uint64_t seed, uint32_t offset,
+                   const fa_layout* layout, int dtype, void* stream);
+
+/* The backward of fa_fwd_strided (the same mask, dropout and, for q, k, v,
+ * o, the same tensors): dq, dk, dv written through their strides in
+ * `layout` (row strides at least d); dO read through its strides.  The
+ * workspace (fa_bwd_workspace_size) is always packed.  Everything else as
+ * fa_bwd. */
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const int32_t* key_len, const uint8_t* block_mask, int block_size,
+                   float dropout_p, uint64_t seed, uint32_t offset,
+                   const fa_layout* layout, void* workspace, size_t workspace_bytes,
+                   int dtype, void* stream);
 
 /* Bytes of device workspace fa_decode needs: one partial result (d + 2
  * floats) per (b, h, query, key chunk), the keys split into chunks of 256 to

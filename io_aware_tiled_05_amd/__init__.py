@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import math
 
+from ._lib import FaLayout, FaStrides
 from ._lib import (FA_BF16, FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ,  # noqa: F401
                    FA_BWD_STAGE_GRADS,  # noqa: F401
                    FA_ERR_HIP, FA_ERR_INVALID, FA_ERR_TOO_LARGE, FA_ERR_UNSUPPORTED,  # noqa: F401
@@ -27,7 +28,8 @@ from ._lib import (FA_BF16, FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ, 
 
 __all__ = ["fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_fwd_blocksparse", "fa_bwd_blocksparse",
            "fa_bwd_stage", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size",
-           "fa_fwd_dropout", "fa_bwd_dropout", "FaError", "load"]
+           "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_strided", "fa_bwd_strided", "FaError",
+           "load"]
 
 
 def _torch():
@@ -340,4 +342,127 @@ def fa_bwd_dropout(q, k, v, o, lse, dO, dropout_p, seed, offset=0, scale=None, c
                _dtype_code(q), _stream(stream, q))
     check("fa_bwd_dropout", st)
     _keep(stream, q, kl, *made)
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Strided views (fa_fwd_strided, fa_bwd_strided)
+# ---------------------------------------------------------------------------
+
+def _view_ok(t):
+    """Whether the kernels can read or write the [B, H, N, d] view t in
+    place: d contiguous, every other stride and the base 16-byte aligned."""
+    align = 16 // t.element_size()
+    st = t.stride()
+    return (st[3] == 1 and all(x >= 0 and x % align == 0 for x in st[:3])
+            and t.data_ptr() % 16 == 0 and st[2] < (1 << 24))
+
+
+def _as_view(t):
+    """t itself when the kernels take it in place, else a packed copy (a
+    layout they cannot address: d not contiguous, or unaligned strides)."""
+    return t if _view_ok(t) else t.contiguous()
+
+
+def _check_views(*ts):
+    """Tensors of q's shape, dtype and device (any strides)."""
+    q = ts[0]
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    for t in ts:
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, dO and the gradients must share shape and dtype")
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("tensors must be on the same GPU")
+
+
+def _strides(t):
+    return FaStrides(*t.stride()[:3]) if t is not None else FaStrides(0, 0, 1)
+
+
+def _layout(q=None, k=None, v=None, o=None, dO=None, dq=None, dk=None, dv=None):
+    return FaLayout(*(_strides(t) for t in (q, k, v, o, dO, dq, dk, dv)))
+
+
+def _out_view(like, out):
+    """The caller's output view (checked: writable in place, rows apart), or
+    a new tensor with like's memory order (a [B, N, H, d]-ordered input gives
+    a [B, N, H, d]-ordered output)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(like)  # keeps the stride order of dense views
+        if not _view_ok(out):
+            out = torch.empty(like.shape, dtype=like.dtype, device=like.device)
+        return out, [out]
+    _check_views(like, out)
+    if not _view_ok(out) or out.stride(2) < out.shape[3]:
+        raise ValueError("output views need a contiguous d, 16-byte aligned strides and rows "
+                         "at least d elements apart")
+    return out, []
+
+
+def _mask_args(q, causal, key_len, block_mask, block_size):
+    kl = _key_len(key_len, q)
+    bm = None if block_mask is None else _block_mask(block_mask, q, block_size)
+    if bm is not None and (causal or kl is not None):
+        raise ValueError("block_mask is not combined with causal or key_len")
+    return kl, bm
+
+
+def fa_fwd_strided(q, k, v, scale=None, causal=False, key_len=None, block_mask=None,
+                   block_size=128, dropout_p=0.0, seed=0, offset=0, out=None, lse=None,
+                   stream=None):
+    """The forward on [B, H, N, d] views of any strides (e.g. the transpose of
+    [B, N, H, d] activations), read and written in place; every mask and
+    dropout option in one call.  See include/fa.h (fa_fwd_strided).
+    Returns (O, lse); O has q's memory order unless `out` is given."""
+    torch = _torch()
+    _check_views(q, k, v)
+    q, k, v = (_as_view(t) for t in (q, k, v))
+    B, H, N, d = q.shape
+    kl, bm = _mask_args(q, causal, key_len, block_mask, block_size)
+    sd, off = _seed(seed, offset)
+    o, made = _out_view(q, out)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        made.append(lse)
+    _check_lse(lse, q)
+    lay = _layout(q=q, k=k, v=v, o=o)
+    st = _call(q, "fa_fwd_strided", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+               _scale(scale, d), int(bool(causal)), _ptr(kl), _ptr(bm), block_size,
+               float(dropout_p), sd, off, lay, _dtype_code(q), _stream(stream, q))
+    check("fa_fwd_strided", st)
+    _keep(stream, q, kl, bm, *made)
+    return o, lse
+
+
+def fa_bwd_strided(q, k, v, o, lse, dO, scale=None, causal=False, key_len=None, block_mask=None,
+                   block_size=128, dropout_p=0.0, seed=0, offset=0, dq=None, dk=None, dv=None,
+                   workspace=None, stream=None):
+    """The backward of fa_fwd_strided on views of any strides; dq, dk, dv
+    take the memory order of q, k, v unless given.  See include/fa.h
+    (fa_bwd_strided).  Returns (dq, dk, dv)."""
+    torch = _torch()
+    _check_views(q, k, v, o, dO)
+    q, k, v, o, dO = (_as_view(t) for t in (q, k, v, o, dO))
+    _check_lse(lse, q)
+    B, H, N, d = q.shape
+    kl, bm = _mask_args(q, causal, key_len, block_mask, block_size)
+    sd, off = _seed(seed, offset)
+    dq, m1 = _out_view(q, dq)
+    dk, m2 = _out_view(k, dk)
+    dv, m3 = _out_view(v, dv)
+    made = m1 + m2 + m3
+    need = fa_bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+        made.append(workspace)
+    _check_workspace(workspace, q, need)
+    lay = _layout(q=q, k=k, v=v, o=o, dO=dO, dq=dq, dk=dk, dv=dv)
+    st = _call(q, "fa_bwd_strided", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+               _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)),
+               _ptr(kl), _ptr(bm), block_size, float(dropout_p), sd, off, lay, _ptr(workspace),
+               workspace.numel() * workspace.element_size(), _dtype_code(q), _stream(stream, q))
+    check("fa_bwd_strided", st)
+    _keep(stream, q, kl, bm, *made)
     return dq, dk, dv

@@ -16,8 +16,21 @@ FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, -1,
 FA_NOALLOC_SCRATCH_BYTES = 128 << 20
 FA_BWD_STAGE_D, FA_BWD_STAGE_DKDV, FA_BWD_STAGE_DQ, FA_BWD_STAGE_GRADS = 1, 2, 3, 4
 
+
+
+class FaStrides(C.Structure):
+    """fa_strides: element strides (batch, head, row) of a [B][H][N][d] view."""
+    _fields_ = [("batch", C.c_int64), ("head", C.c_int64), ("row", C.c_int64)]
+
+
+class FaLayout(C.Structure):
+    """fa_layout: the strides of every tensor of a call."""
+    _fields_ = [(n, FaStrides) for n in ("q", "k", "v", "o", "dO", "dq", "dk", "dv")]
+
+
 # (name, restype, argtypes) for every function in include/fa.h
 _P, _I, _F, _SZ = C.c_void_p, C.c_int, C.c_float, C.c_size_t
+_LP = C.POINTER(FaLayout)
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _P]),
     "fa_bwd_workspace_size": (_SZ, [_I, _I, _I, _I]),
@@ -36,6 +49,10 @@ SIGNATURES = {
     "fa_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _I, _P]),
     "fa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I,
                             _P]),
+    "fa_fwd_strided": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _I, _F,
+                            C.c_uint64, C.c_uint32, _LP, _I, _P]),
+    "fa_bwd_strided": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P,
+                            _I, _F, C.c_uint64, C.c_uint32, _LP, _P, _SZ, _I, _P]),
     "fa_status_string": (C.c_char_p, [_I]),
 }
 

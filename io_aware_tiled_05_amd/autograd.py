@@ -1,7 +1,8 @@
 """Differentiable exact attention on the HIP kernels.
 
-``attention`` and ``scaled_dot_product_attention`` wrap ``fa_fwd`` /
-``fa_bwd`` (and their block-sparse forms) in a ``torch.autograd.Function``:
+``attention`` and ``scaled_dot_product_attention`` wrap ``fa_fwd_strided``
+/ ``fa_bwd_strided`` (every mask and dropout option of the library) in a
+``torch.autograd.Function``:
 the forward saves q, k, v, O and the per-row log-sum-exp, and the backward
 recomputes the probabilities from them on the GPU ([ODP] "FlashAttention:
 Fast and Memory-Efficient Exact Attention with IO-Awareness", section "The
@@ -13,17 +14,17 @@ the forward's mask from its seed instead of storing it.
 
 Like the rest of the binding this only marshals tensors: every step of the
 computation runs in ``libfa.so``; there is no PyTorch fallback.  The
-kernels take contiguous ``[B, H, N, d]`` tensors; the ``[B, N, H, d]``
-layout (``layout="bnhd"``) is accepted and copied to it on the way in (and
-the gradients back).
+kernels read and write strided views in place (``fa_fwd_strided``,
+``fa_bwd_strided``), so the ``[B, N, H, d]`` layout (``layout="bnhd"``) and
+non-contiguous SDPA inputs reach them without transposing copies; the
+output and the gradients keep the inputs' memory order.
 """
 
 from __future__ import annotations
 
 import torch
 
-from . import (fa_bwd, fa_bwd_blocksparse, fa_bwd_dropout, fa_fwd, fa_fwd_blocksparse,
-               fa_fwd_dropout)
+from . import fa_bwd_strided, fa_fwd_strided
 
 __all__ = ["FlashAttention", "attention", "scaled_dot_product_attention"]
 
@@ -33,38 +34,26 @@ class FlashAttention(torch.autograd.Function):
     ``key_len`` (keys j >= key_len[b] hidden) or a 128x128 ``block_mask``,
     and optionally dropout on the probabilities (``dropout`` = (p, seed,
     offset); the backward regenerates the same mask from them).
-    q, k, v: contiguous [B, H, N, d] fp32, fp16 or bf16 (block_mask and
-    dropout: fp16 or bf16)."""
+    q, k, v: [B, H, N, d] views of any strides with a contiguous d, fp32,
+    fp16 or bf16 (block_mask and dropout: fp16 or bf16)."""
 
     @staticmethod
     def forward(ctx, q, k, v, scale, causal, key_len, block_mask, dropout):
-        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        if block_mask is not None:
-            o, lse = fa_fwd_blocksparse(q, k, v, block_mask, scale=scale)
-        elif dropout is not None:
-            p, seed, offset = dropout
-            o, lse = fa_fwd_dropout(q, k, v, p, seed, offset, scale=scale, causal=causal,
-                                    key_len=key_len)
-        else:
-            o, lse = fa_fwd(q, k, v, scale=scale, causal=causal, key_len=key_len)
+        p, seed, offset = dropout if dropout is not None else (0.0, 0, 0)
+        o, lse = fa_fwd_strided(q, k, v, scale=scale, causal=causal, key_len=key_len,
+                                block_mask=block_mask, dropout_p=p, seed=seed, offset=offset)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.scale, ctx.causal, ctx.key_len, ctx.block_mask = scale, causal, key_len, block_mask
-        ctx.dropout = dropout
+        ctx.dropout = (p, seed, offset)
         return o
 
     @staticmethod
     def backward(ctx, dO):
         q, k, v, o, lse = ctx.saved_tensors
-        dO = dO.contiguous()
-        if ctx.block_mask is not None:
-            dq, dk, dv = fa_bwd_blocksparse(q, k, v, o, lse, dO, ctx.block_mask, scale=ctx.scale)
-        elif ctx.dropout is not None:
-            p, seed, offset = ctx.dropout
-            dq, dk, dv = fa_bwd_dropout(q, k, v, o, lse, dO, p, seed, offset, scale=ctx.scale,
-                                        causal=ctx.causal, key_len=ctx.key_len)
-        else:
-            dq, dk, dv = fa_bwd(q, k, v, o, lse, dO, scale=ctx.scale, causal=ctx.causal,
-                                key_len=ctx.key_len)
+        p, seed, offset = ctx.dropout
+        dq, dk, dv = fa_bwd_strided(q, k, v, o, lse, dO, scale=ctx.scale, causal=ctx.causal,
+                                    key_len=ctx.key_len, block_mask=ctx.block_mask,
+                                    dropout_p=p, seed=seed, offset=offset)
         return dq, dk, dv, None, None, None, None, None
 
 

@@ -57,13 +57,35 @@ int make_dropout(float p, uint64_t seed, uint32_t offset, fa::Dropout* out) {
   return FA_OK;
 }
 
+// One tensor view's strides: non-negative; the row, head and batch strides
+// keep every row's start 16-byte aligned (the kernels move rows in 16-byte
+// chunks); row strides below 2^24 elements (tile offsets are 32-bit); an
+// output's rows must not overlap (row stride >= d).
+bool strides_ok(const fa::Strides& s, int d, int dtype, bool output) {
+  const int64_t align = dtype == FA_F32 ? 4 : 8;  // elements per 16 bytes
+  if (s.b < 0 || s.h < 0 || s.n < 1 || s.n >= (int64_t(1) << 24)) return false;
+  if (s.b % align || s.h % align || s.n % align) return false;
+  if (output && s.n < d) return false;
+  return s.b < (int64_t(1) << 46) && s.h < (int64_t(1) << 46);
+}
+
+fa::Layout layout_of(const fa_layout* l, int H, int N, int d) {
+  if (!l) return fa::packed_layout(H, N, d);
+  auto cv = [](const fa_strides& s) { return fa::Strides{s.batch, s.head, s.row}; };
+  return {cv(l->q), cv(l->k), cv(l->v), cv(l->o), cv(l->dO), cv(l->dq), cv(l->dk), cv(l->dv)};
+}
+
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                int H, int N, int d, float scale, int causal, const int32_t* key_len,
                const uint8_t* block_mask, int dtype, void* stream,
-               const fa::Dropout& drop = fa::Dropout{}) {
+               const fa::Dropout& drop = fa::Dropout{}, const fa_layout* layout = nullptr) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  const fa::Layout lay = layout_of(layout, H, N, d);
+  if (!strides_ok(lay.q, d, dtype, false) || !strides_ok(lay.k, d, dtype, false) ||
+      !strides_ok(lay.v, d, dtype, false) || !strides_ok(lay.o, d, dtype, true))
+    return FA_ERR_INVALID;
   int st = check_dtype(dtype);
   if (st == FA_OK) st = check_scale(scale);
   if (st == FA_OK) st = check_sizes(B, H, N, d);
@@ -71,7 +93,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   if (block_mask && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (drop.on && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, dtype,
-                static_cast<hipStream_t>(stream), drop};
+                static_cast<hipStream_t>(stream), drop, lay};
   return hip_status(fa::launch_fwd(a));
 }
 
@@ -79,16 +101,28 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                float scale, int causal, const int32_t* key_len, const uint8_t* block_mask,
                void* workspace, size_t workspace_bytes, int dtype, void* stream,
-               int stage, const fa::Dropout& drop = fa::Dropout{}) {
+               int stage, const fa::Dropout& drop = fa::Dropout{},
+               const fa_layout* layout = nullptr) {
   if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID;
+  const fa::Layout lay = layout_of(layout, H, N, d);
   const int st = fa::bwd_check(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal,
-                               block_mask != nullptr, dtype, drop.on != 0);
+                               block_mask != nullptr, dtype, drop.on != 0, &lay);
   if (st != FA_OK) return st;
   if (workspace_bytes < fa_bwd_workspace_size(B, H, N, d)) return FA_ERR_INVALID;
   fa::BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
                 block_mask, workspace, dtype,
-                static_cast<hipStream_t>(stream), drop};
+                static_cast<hipStream_t>(stream), drop, lay};
   return hip_status(fa::launch_bwd(a, stage));
+}
+
+// the mask arguments of the strided entry points: a block mask excludes
+// causal, key lengths and dropout, and needs 128-row blocks
+int mask_check(int causal, const int32_t* key_len, const uint8_t* block_mask, int block_size,
+               float dropout_p) {
+  if (!block_mask) return FA_OK;
+  if (causal || key_len || dropout_p != 0.f) return FA_ERR_INVALID;
+  if (block_size != 128) return block_size < 1 ? FA_ERR_INVALID : FA_ERR_UNSUPPORTED;
+  return FA_OK;
 }
 
 }  // namespace
@@ -98,12 +132,17 @@ namespace fa {
 int bwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
               const void* dO, const void* dq, const void* dk, const void* dv, int B, int H,
               int N, int d, float scale, int causal, bool block_sparse, int dtype,
-              bool dropout) {
+              bool dropout, const Layout* lay) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return FA_ERR_INVALID;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (lay && (!strides_ok(lay->q, d, dtype, false) || !strides_ok(lay->k, d, dtype, false) ||
+              !strides_ok(lay->v, d, dtype, false) || !strides_ok(lay->o, d, dtype, false) ||
+              !strides_ok(lay->dO, d, dtype, false) || !strides_ok(lay->dq, d, dtype, true) ||
+              !strides_ok(lay->dk, d, dtype, true) || !strides_ok(lay->dv, d, dtype, true)))
+    return FA_ERR_INVALID;
   int st = check_dtype(dtype);
   if (st == FA_OK) st = check_scale(scale);
   if (st == FA_OK) st = check_sizes(B, H, N, d);
@@ -206,6 +245,34 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
   if (st != FA_OK) return st;
   return bwd_common(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
                     nullptr, workspace, workspace_bytes, dtype, stream, 0, dr);
+}
+
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int N, int d, float scale, int causal, const int32_t* key_len,
+                   const uint8_t* block_mask, int block_size, float dropout_p, uint64_t seed,
+                   uint32_t offset, const fa_layout* layout, int dtype, void* stream) {
+  int st = mask_check(causal, key_len, block_mask, block_size, dropout_p);
+  if (st != FA_OK) return st;
+  fa::Dropout dr;
+  st = make_dropout(dropout_p, seed, offset, &dr);
+  if (st != FA_OK) return st;
+  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, causal, key_len, block_mask, dtype,
+                    stream, dr, layout);
+}
+
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   float scale, int causal, const int32_t* key_len, const uint8_t* block_mask,
+                   int block_size, float dropout_p, uint64_t seed, uint32_t offset,
+                   const fa_layout* layout, void* workspace, size_t workspace_bytes, int dtype,
+                   void* stream) {
+  int st = mask_check(causal, key_len, block_mask, block_size, dropout_p);
+  if (st != FA_OK) return st;
+  fa::Dropout dr;
+  st = make_dropout(dropout_p, seed, offset, &dr);
+  if (st != FA_OK) return st;
+  return bwd_common(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, key_len,
+                    block_mask, workspace, workspace_bytes, dtype, stream, 0, dr, layout);
 }
 
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d) {

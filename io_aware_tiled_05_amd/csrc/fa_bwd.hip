@@ -191,10 +191,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
                                                       const uint16_t* k, const uint16_t* v,
                                                       float* Dbuf, float* shift,
                                                       uint32_t* part, int N, int BH,
-                                                      int iters) {
+                                                      int iters, int H, Layout lay) {
   constexpr int TPR = pre_tpr<D>();  // threads per row, 8 elements (16 B) each
   constexpr int RPB = 256 / TPR;      // rows per pass of the workgroup
   const int bh = blockIdx.x;
+  const int b = bh / H, hd = bh - b * H;
+  o += b * lay.o.b + hd * lay.o.h;
+  dO += b * lay.dO.b + hd * lay.dO.h;
+  q += b * lay.q.b + hd * lay.q.h;
+  k += b * lay.k.b + hd * lay.k.h;
+  v += b * lay.v.b + hd * lay.v.h;
   const int c = (int)(threadIdx.x % TPR) * 8;
   const bool col_ok = c < D;
   uint32_t mx[4] = {0u, 0u, 0u, 0u};
@@ -206,17 +212,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
     const int64_t row = (int64_t)bh * N + r;
     float s = 0.f;
     if (ok && col_ok) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + c);
-      const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + c);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(o + r * lay.o.n + c);
+      const u32x4 g = *reinterpret_cast<const u32x4*>(dO + r * lay.dO.n + c);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         s = fmaf(to_f32<T>(a[j] & 0xffffu), to_f32<T>(g[j] & 0xffffu), s);
         s = fmaf(to_f32<T>(a[j] >> 16), to_f32<T>(g[j] >> 16), s);
       }
       if (STATS) {
-        const uint32_t m0 = absmax8<T>(*reinterpret_cast<const u32x4*>(q + row * D + c));
-        const uint32_t m1 = absmax8<T>(*reinterpret_cast<const u32x4*>(k + row * D + c));
-        const uint32_t m2 = absmax8<T>(*reinterpret_cast<const u32x4*>(v + row * D + c));
+        const uint32_t m0 = absmax8<T>(*reinterpret_cast<const u32x4*>(q + r * lay.q.n + c));
+        const uint32_t m1 = absmax8<T>(*reinterpret_cast<const u32x4*>(k + r * lay.k.n + c));
+        const uint32_t m2 = absmax8<T>(*reinterpret_cast<const u32x4*>(v + r * lay.v.n + c));
         const uint32_t m3 = absmax8<T>(g);
         mx[0] = mx[0] > m0 ? mx[0] : m0;
         mx[1] = mx[1] > m1 ? mx[1] : m1;
@@ -272,10 +278,16 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, con
                                                           uint16_t* q16, uint16_t* k16,
                                                           uint16_t* do16, float* nDs, float* nsh,
                                                           int N, int BH, int rbph, int iters,
-                                                          int rexp) {
+                                                          int rexp, int H, Layout lay) {
   constexpr int TPR = D / 8;       // threads per row, 16 bytes each
   constexpr int RPB = 256 / TPR;   // rows per workgroup (d = 96: 21, 4 threads idle)
   const int bh = (int)(blockIdx.x / (unsigned)rbph), rb = (int)(blockIdx.x % (unsigned)rbph);
+  {
+    const int b = bh / H, hd = bh - b * H;
+    q += b * lay.q.b + hd * lay.q.h;
+    k += b * lay.k.b + hd * lay.k.h;
+    dO += b * lay.dO.b + hd * lay.dO.h;
+  }
   const int lane = threadIdx.x & 63;
   uint32_t mx[4];
 #pragma unroll
@@ -302,9 +314,9 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, con
     const int r = (rb * iters + it) * RPB + (int)(threadIdx.x / TPR);
     if (r >= N) return;
     const int64_t row = (int64_t)bh * N + r;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(q + row * D + col);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + col);
-    const u32x4 kk = *reinterpret_cast<const u32x4*>(k + row * D + col);
+    const u32x4 a = *reinterpret_cast<const u32x4*>(q + r * lay.q.n + col);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + r * lay.dO.n + col);
+    const u32x4 kk = *reinterpret_cast<const u32x4*>(k + r * lay.k.n + col);
     u32x4 ra, rg, rk;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -351,6 +363,9 @@ struct BwdParams {
   const int32_t* key_len;
   const uint8_t* block_mask;
   int nblk;
+  // element strides of the caller's k, v, dO, dq, dk, dv (q, o are read
+  // only by the D pass; the workspace copies are packed [BH][N][d])
+  Strides sk, sv, sdO, sdq, sdk, sdv;
 };
 
 // B operand (P or dS, 16 keys or queries of chunk a) from a 32x32
@@ -426,8 +441,8 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
   int rank, bh;
   map_workgroup(wg, p.ntiles, p.BH, p.period, &rank, &bh);
   const int kt = rank;  // causal: the lowest key tiles see the most queries, so go first
-  const int b = bh / p.H, N = p.N;
-  const size_t base = (size_t)bh * N * D;
+  const int b = bh / p.H, hd = bh - b * p.H, N = p.N;
+  const size_t base = (size_t)bh * N * D;  // the packed workspace copies
   const uint16_t* Q = p.q16 + base;    // c Q 2^-eq
   const uint16_t* dO = p.do16 + base;  // dO 2^-eo
   const float* nsh = p.nsh + (size_t)bh * N;
@@ -439,10 +454,12 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
 
   // this wave's keys and values as B operands (lane = key, k = d values)
   vec8 kf[KS], vf[KS];
+  const uint16_t* const Kin = p.k + b * p.sk.b + hd * p.sk.h;
+  const uint16_t* const Vin = p.v + b * p.sv.b + hd * p.sv.h;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    u32x4 kr = ldg16(p.k + base + (size_t)key * D + ks * 16 + h * 8, key < N);
-    u32x4 vr = ldg16(p.v + base + (size_t)key * D + ks * 16 + h * 8, key < N);
+    u32x4 kr = ldg16(Kin + (int64_t)key * p.sk.n + ks * 16 + h * 8, key < N);
+    u32x4 vr = ldg16(Vin + (int64_t)key * p.sv.n + ks * 16 + h * 8, key < N);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       kr[j] = Elt<TI>::pack2(ldexpf(to_f32<T>(kr[j] & 0xffffu), -ek),
@@ -469,7 +486,7 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
     for (int db = 0; db < DB; ++db)
       toff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec, db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
 
-  const TileCopy<D, kBQ, NW> copy(wave, lane);
+  const TileCopy<D, kBQ, NW> copy(wave, lane, D);  // the packed copies of Q and dO
   const bool any_key = kw < L;  // every key of this wave padded away -> zero gradients
 
   auto compute = [&](const uint16_t* tq, const uint16_t* to, const float* tl, const float* td,
@@ -646,19 +663,21 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
     const int rx = DROP ? p.drop.rexp : 0;
     const int ekk = sc.eq + sc.eo + sc.ev + rx;
     const float kmul = sc.exact ? p.scale : kLn2;
+    uint16_t* const dKo = p.dk + b * p.sdk.b + hd * p.sdk.h + (int64_t)key * p.sdk.n;
+    uint16_t* const dVo = p.dv + b * p.sdv.b + hd * p.sdv.h + (int64_t)key * p.sdv.n;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const size_t off = base + (size_t)key * D + db * 32 + 8 * i + 4 * h;
+        const int off = db * 32 + 8 * i + 4 * h;
         f32x4 k4, v4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           k4[j] = ldexpf(dk[db][4 * i + j] * kmul, ekk);
           v4[j] = ldexpf(dv[db][4 * i + j], sc.eo + rx);
         }
-        *reinterpret_cast<u32x2*>(p.dk + off) = pack4<T>(k4);
-        *reinterpret_cast<u32x2*>(p.dv + off) = pack4<T>(v4);
+        *reinterpret_cast<u32x2*>(dKo + off) = pack4<T>(k4);
+        *reinterpret_cast<u32x2*>(dVo + off) = pack4<T>(v4);
       }
   }
 }
@@ -701,10 +720,10 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
   int rank, bh;
   map_workgroup(wg, p.ntiles, p.BH, p.period, &rank, &bh);
   const int qt = CAUSAL ? p.ntiles - 1 - rank : rank;  // longest rows first
-  const int b = bh / p.H, N = p.N;
-  const size_t base = (size_t)bh * N * D;
+  const int b = bh / p.H, hd = bh - b * p.H, N = p.N;
+  const size_t base = (size_t)bh * N * D;  // the packed workspace copies
   const uint16_t* K = p.k16 + base;  // K 2^-ek, fp16
-  const uint16_t* V = p.v + base;
+  const uint16_t* V = p.v + b * p.sv.b + hd * p.sv.h;
   const int L = valid_keys(p.key_len, b, N);
   const int q0 = qt * kBR, qw = q0 + wave * 32, query = qw + l32;
   const Scales sc = bwd_scales<D>(p.maxes, p.BH, bh, p.c);
@@ -726,10 +745,11 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
   hvec8 qf[KS];
   vec8 of[KS];
   const bool qok = query < N;
+  const uint16_t* const dOin = p.dO + b * p.sdO.b + hd * p.sdO.h + (int64_t)query * p.sdO.n;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     qf[ks] = as_vec8<TI>(ldg16(p.q16 + base + (size_t)query * D + ks * 16 + h * 8, qok));
-    of[ks] = as_vec8<T>(ldg16(p.dO + base + (size_t)query * D + ks * 16 + h * 8, qok));
+    of[ks] = as_vec8<T>(ldg16(dOin + ks * 16 + h * 8, qok));
   }
   // the row terms of this lane's query (-shift 2^-f for the scores, -D for
   // dP; dropout subtracts D after the mask instead), replicated: every
@@ -765,7 +785,9 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
     for (int db = 0; db < DB; ++db)
       toff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec, db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
 
-  const TileCopy<D, kBC, NW> copy(wave, lane);
+  // chunk offsets for the packed K copy; V's tiles adjust them when its
+  // row stride is not d
+  const TileCopy<D, kBC, NW> copy(wave, lane, D);
 
   // `prefetch` starts the copies of the next tile; it runs inside the
   // compute, after the score products are issued, so that the copies (which
@@ -857,7 +879,7 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
   auto walk = [&](int ntiles, auto key0) __attribute__((always_inline)) {
     if (ntiles <= 0) return;
     copy(K, key0(0), N, sK0);
-    copy(V, key0(0), N, sV0);
+    copy.copy_rs(V, p.sv.n, key0(0), N, sV0);
     auto step = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv)
         __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -866,7 +888,7 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
         if (t + 1 < ntiles) {
           const int k1 = key0(t + 1);
           copy(K, k1, N, nk);
-          copy(V, k1, N, nv);
+          copy.copy_rs(V, p.sv.n, k1, N, nv);
         }
       };
       compute(ck, cv, key0(t), prefetch);
@@ -897,6 +919,7 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
 
   if (qok) {  // dQ = scale 2^(ek - kq + rexp) (dS' K')
     const int eqo = sc.ek - kq + (DROP ? p.drop.rexp : 0);
+    uint16_t* const dQo = p.dq + b * p.sdq.b + hd * p.sdq.h + (int64_t)query * p.sdq.n;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -904,8 +927,7 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
         f32x4 q4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) q4[j] = ldexpf(acc[db][4 * i + j] * p.scale, eqo);
-        *reinterpret_cast<u32x2*>(p.dq + base + (size_t)query * D + db * 32 + 8 * i + 4 * h) =
-            pack4<T>(q4);
+        *reinterpret_cast<u32x2*>(dQo + db * 32 + 8 * i + 4 * h) = pack4<T>(q4);
       }
   }
 }
@@ -947,7 +969,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_fused_kernel(BwdPara
 #define FA_BWD_INSTANTIATE(T, D)                                                  \
   template __global__ void bwd_pre_kernel<T, D, true>(                            \
       const uint16_t*, const uint16_t*, const float*, const uint16_t*, const uint16_t*, \
-      const uint16_t*, float*, float*, uint32_t*, int, int, int);                   \
+      const uint16_t*, float*, float*, uint32_t*, int, int, int, int, Layout);      \
   template __global__ void bwd_dkdv_kernel<T, D, true, false, false>(BwdParams);   \
   template __global__ void bwd_dkdv_kernel<T, D, false, false, false>(BwdParams);  \
   template __global__ void bwd_dkdv_kernel<T, D, false, true, false>(BwdParams);   \
@@ -966,7 +988,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_fused_kernel(BwdPara
   template __global__ void bwd_convert_kernel<T, D>(                               \
       const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*,   \
       const uint32_t*, int, uint32_t*, float,                                        \
-      uint16_t*, uint16_t*, uint16_t*, float*, float*, int, int, int, int, int);
+      uint16_t*, uint16_t*, uint16_t*, float*, float*, int, int, int, int, int, int, Layout);
 FA_BWD_INSTANTIATE(__bf16, 32)
 FA_BWD_INSTANTIATE(__bf16, 64)
 FA_BWD_INSTANTIATE(__bf16, 96)
@@ -1010,7 +1032,7 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
     hipLaunchKernelGGL((bwd_pre_kernel<T, D, true>), dim3(BH, nchunk), dim3(256), 0, a.stream,
                        static_cast<const uint16_t*>(a.o), dO, a.lse, q,
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), Dbuf,
-                       shift, part, a.N, BH, iters);
+                       shift, part, a.N, BH, iters, a.H, a.lay);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // convert: row blocks per workgroup so that the grid stays near 4096
@@ -1023,7 +1045,7 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
     hipLaunchKernelGGL((bwd_convert_kernel<T, D>), dim3((unsigned)((int64_t)BH * rbph)),
                        dim3(256), 0, a.stream, q, static_cast<const uint16_t*>(a.k), dO, Dbuf,
                        shift, part, nchunk, maxes, c, q16, k16, do16, nDs, nsh, a.N, BH, rbph,
-                       citers, a.drop.on ? a.drop.rexp : 0);
+                       citers, a.drop.on ? a.drop.rexp : 0, a.H, a.lay);
     e = hipGetLastError();
     if (e != hipSuccess || stage == 1) return e;
   }
@@ -1054,6 +1076,12 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   p.nblk = (a.N + 127) / 128;
   p.period = (FA_BWD_SNAKE && CAUSAL) ? snake_period(p.BH) : 0;
   p.drop = a.drop;
+  p.sk = a.lay.k;
+  p.sv = a.lay.v;
+  p.sdO = a.lay.dO;
+  p.sdq = a.lay.dq;
+  p.sdk = a.lay.dk;
+  p.sdv = a.lay.dv;
 
   if (stage == 0 || stage == 4) {
     p.ntiles = (a.N + kBKV - 1) / kBKV;

@@ -41,6 +41,7 @@ struct Params {
   int H, N, BH, ntiles;
   float c, scale;  // c = scale log2(e)
   const int32_t* key_len;
+  Layout lay;  // element strides of the caller's tensors (D and shift are packed)
 };
 
 __device__ __forceinline__ int valid_keys(const int32_t* key_len, int b, int N) {
@@ -58,15 +59,18 @@ __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
 template <int D>
 __global__ __launch_bounds__(256) void pre_kernel(const float* o, const float* dO,
                                                   const float* lse, float* Dbuf, float* shift,
-                                                  int64_t rows) {
+                                                  int64_t rows, int H, int N, Layout lay) {
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   float s = 0.f;
   if (row < rows) {
+    const int64_t bh = row / N, r = row - bh * N, b = bh / H, hd = bh - b * H;
+    const float* orow = o + b * lay.o.b + hd * lay.o.h + r * lay.o.n;
+    const float* grow = dO + b * lay.dO.b + hd * lay.dO.h + r * lay.dO.n;
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
       const int c = sub + 16 * j;
-      s = fmaf(o[row * D + c], dO[row * D + c], s);
+      s = fmaf(orow[c], grow[c], s);
     }
   }
   s += __shfl_xor(s, 1);
@@ -80,13 +84,20 @@ __global__ __launch_bounds__(256) void pre_kernel(const float* o, const float* d
   }
 }
 
-// rows r0 .. r0 + 63 of a [N][D] matrix into LDS (row stride D + 1), zeros past N
+// rows r0 .. r0 + 63 of a matrix with D elements per row and row stride rs
+// into LDS (row stride D + 1), zeros past N
 template <int D>
-__device__ __forceinline__ void load_tile(const float* g, int r0, int N, float* s, int tid) {
+__device__ __forceinline__ void load_tile(const float* g, int64_t rs, int r0, int N, float* s,
+                                          int tid) {
   for (int c = tid; c < kT * D; c += 256) {
     const int r = c / D, col = c % D;
-    s[r * (D + 1) + col] = r0 + r < N ? g[(size_t)(r0 + r) * D + col] : 0.f;
+    s[r * (D + 1) + col] = r0 + r < N ? g[(int64_t)(r0 + r) * rs + col] : 0.f;
   }
+}
+
+__device__ __forceinline__ int64_t head_offset(const Strides& s, int bh, int H) {
+  const int b = bh / H;
+  return b * s.b + (bh - b * H) * s.h;
 }
 
 template <int D, bool CAUSAL>
@@ -98,16 +109,19 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   int rank, bh;
   map_workgroup(blockIdx.x, p.ntiles, p.BH, 0, &rank, &bh);
   const int b = bh / p.H, N = p.N;
-  const size_t base = (size_t)bh * N * D;
   const int L = valid_keys(p.key_len, b, N);
   const int k0 = rank * kT, key = k0 + wave * 16 + n;
+  const float* const Q = p.q + head_offset(p.lay.q, bh, p.H);
+  const float* const dOt = p.dO + head_offset(p.lay.dO, bh, p.H);
 
   // this wave's 16 keys and values as B operands (column n = key, k = d)
   float kf[KS], vf[KS];
+  const float* const krow = p.k + head_offset(p.lay.k, bh, p.H) + (int64_t)key * p.lay.k.n;
+  const float* const vrow = p.v + head_offset(p.lay.v, bh, p.H) + (int64_t)key * p.lay.v.n;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = key < N ? p.k[base + (size_t)key * D + 4 * ks + g] : 0.f;
-    vf[ks] = key < N ? p.v[base + (size_t)key * D + 4 * ks + g] : 0.f;
+    kf[ks] = key < N ? krow[4 * ks + g] : 0.f;
+    vf[ks] = key < N ? vrow[4 * ks + g] : 0.f;
   }
   f32x4 dk[DB], dv[DB];  // dK^T, dV^T: row d = 16 db + 4g + i, column = key
 #pragma unroll
@@ -118,8 +132,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
   for (int t = (k0 < L ? t0 : nqt); t < nqt; ++t) {
     const int q0 = t * kT;
     __syncthreads();
-    load_tile<D>(p.q + base, q0, N, sQ, tid);
-    load_tile<D>(p.dO + base, q0, N, sO, tid);
+    load_tile<D>(Q, p.lay.q.n, q0, N, sQ, tid);
+    load_tile<D>(dOt, p.lay.dO.n, q0, N, sO, tid);
     if (tid < kT) {
       const int r = q0 + tid;
       sD[tid] = r < N ? p.D[(size_t)bh * N + r] : 0.f;
@@ -161,13 +175,15 @@ __global__ __launch_bounds__(256) void dkdv_kernel(Params p) {
       }
   }
   if (key < N) {
+    float* const dkrow = p.dk + head_offset(p.lay.dk, bh, p.H) + (int64_t)key * p.lay.dk.n;
+    float* const dvrow = p.dv + head_offset(p.lay.dv, bh, p.H) + (int64_t)key * p.lay.dv.n;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const size_t off = base + (size_t)key * D + 16 * db + 4 * g + i;
-        p.dk[off] = dk[db][i] * p.scale;
-        p.dv[off] = dv[db][i];
+        const int off = 16 * db + 4 * g + i;
+        dkrow[off] = dk[db][i] * p.scale;
+        dvrow[off] = dv[db][i];
       }
   }
 }
@@ -182,15 +198,18 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
   map_workgroup(blockIdx.x, p.ntiles, p.BH, 0, &rank, &bh);
   const int qt = CAUSAL ? p.ntiles - 1 - rank : rank;  // longest rows first
   const int b = bh / p.H, N = p.N;
-  const size_t base = (size_t)bh * N * D;
   const int L = valid_keys(p.key_len, b, N);
   const int q0 = qt * kT, query = q0 + wave * 16 + n;
+  const float* const K = p.k + head_offset(p.lay.k, bh, p.H);
+  const float* const V = p.v + head_offset(p.lay.v, bh, p.H);
 
   float qf[KS], of[KS];  // B operands: column n = query, k = d
+  const float* const qrow = p.q + head_offset(p.lay.q, bh, p.H) + (int64_t)query * p.lay.q.n;
+  const float* const orow = p.dO + head_offset(p.lay.dO, bh, p.H) + (int64_t)query * p.lay.dO.n;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = query < N ? p.q[base + (size_t)query * D + 4 * ks + g] : 0.f;
-    of[ks] = query < N ? p.dO[base + (size_t)query * D + 4 * ks + g] : 0.f;
+    qf[ks] = query < N ? qrow[4 * ks + g] : 0.f;
+    of[ks] = query < N ? orow[4 * ks + g] : 0.f;
   }
   const float shift = query < N ? p.shift[(size_t)bh * N + query] : pos_inf();
   const float Dq = query < N ? p.D[(size_t)bh * N + query] : 0.f;
@@ -206,8 +225,8 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
   for (int t = 0; t < nkt; ++t) {
     const int kt0 = t * kT;
     __syncthreads();
-    load_tile<D>(p.k + base, kt0, N, sK, tid);
-    load_tile<D>(p.v + base, kt0, N, sV, tid);
+    load_tile<D>(K, p.lay.k.n, kt0, N, sK, tid);
+    load_tile<D>(V, p.lay.v.n, kt0, N, sV, tid);
     __syncthreads();
     // S^T, dP^T: rows = keys 16 kb + 4g + i, column = this lane's query
     f32x4 s[4], dp[4];
@@ -240,16 +259,16 @@ __global__ __launch_bounds__(256) void dq_kernel(Params p) {
       }
   }
   if (query < N) {
+    float* const dqrow = p.dq + head_offset(p.lay.dq, bh, p.H) + (int64_t)query * p.lay.dq.n;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<f32x4*>(p.dq + base + (size_t)query * D + 16 * db + 4 * g) =
-          acc[db] * p.scale;
+      *reinterpret_cast<f32x4*>(dqrow + 16 * db + 4 * g) = acc[db] * p.scale;
   }
 }
 
 #define FA_BWD32_INSTANTIATE(D)                                                        \
   template __global__ void pre_kernel<D>(const float*, const float*, const float*,    \
-                                         float*, float*, int64_t);                     \
+                                         float*, float*, int64_t, int, int, Layout);   \
   template __global__ void dkdv_kernel<D, true>(Params);                               \
   template __global__ void dkdv_kernel<D, false>(Params);                              \
   template __global__ void dq_kernel<D, true>(Params);                                 \
@@ -281,13 +300,14 @@ hipError_t run(const BwdArgs& a, int stage) {
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
   p.key_len = a.key_len;
+  p.lay = a.lay;
   hipError_t e = hipSuccess;
   if (stage == 0 || stage == 1) {
     const int64_t rows = (int64_t)p.BH * a.N;
     hipLaunchKernelGGL((pre_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
                        a.stream, static_cast<const float*>(a.o), p.dO, a.lse,
                        reinterpret_cast<float*>(ws + w.D), reinterpret_cast<float*>(ws + w.shift),
-                       rows);
+                       rows, a.H, a.N, a.lay);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -187,54 +187,70 @@ __host__ __device__ __forceinline__ int tile_off(int r, int c) {
   return r * D + (((c >> 3) ^ swz<D / 8>(r)) << 3) + (c & 7);
 }
 
-// Element offset, relative to row0 * D, that a copy lane reads for the tile
-// element offset `off` (tile row r = off / D) when rows at or past `nrows`
-// re-read row nrows - 1.  Signed: row0 itself may lie past nrows - 1 (the
-// second half of the last 128-row block of a block-sparse list), and the
-// result is then negative.  The row read is min(row0 + r, nrows - 1).
-__host__ __device__ inline int clamped_chunk_offset(uint32_t off, int D, int row0, int nrows) {
-  const int r = (int)(off / (uint32_t)D);
+// Element offset, relative to row0 * rs, that a copy lane reads for the
+// chunk at offset `off` = r * rs + (chunk column) of tile row r, in a matrix
+// of row stride rs, when rows at or past `nrows` re-read row nrows - 1.
+// Signed: row0 itself may lie past nrows - 1 (the second half of the last
+// 128-row block of a block-sparse list), and the result is then negative.
+// The row read is min(row0 + r, nrows - 1).
+__host__ __device__ inline int64_t clamped_chunk_offset(uint32_t off, int r, int64_t rs, int row0,
+                                                        int nrows) {
   const int last = nrows - 1 - row0;  // last valid row, relative to row0
-  return r <= last ? (int)off : (int)off - (r - last) * D;
+  return r <= last ? (int64_t)off : (int64_t)off - (int64_t)(r - last) * rs;
 }
 
-// Copies rows [row0, row0 + ROWS) of a row-major [*][D] 16-bit matrix into
-// a swizzled LDS tile with direct global->LDS loads (no VGPR staging).  NW
-// waves share the copy: 16-byte slot s of the tile (slot = 64 * instruction
-// + lane) receives row s / CPR, chunk (s % CPR) ^ swz(row).  The per-lane
-// element offsets are tile-invariant and computed once; a copy is then one
-// load per instruction from a wave-uniform base.  Rows at or past `nrows`
-// re-read row nrows-1 (their contents are never used unmasked).
-// Completion is tracked by vmcnt.
+// Copies rows [row0, row0 + ROWS) of a row-major 16-bit matrix with D
+// elements per row and a row stride of rs elements (rs = D when the rows
+// are packed; a multiple of 8) into a swizzled LDS tile with direct
+// global->LDS loads (no VGPR staging).  NW waves share the copy: 16-byte
+// slot s of the tile (slot = 64 * instruction + lane) receives row s / CPR,
+// chunk (s % CPR) ^ swz(row).  The per-lane element offsets are
+// tile-invariant and computed once for the row stride given at
+// construction; a copy is then one load per instruction from a
+// wave-uniform base.  A copy from a matrix of another row stride (copy_rs)
+// adjusts the offsets on the way, a few instructions per chunk.  Rows at or
+// past `nrows` re-read row nrows-1 (their contents are never used
+// unmasked).  Completion is tracked by vmcnt.
 template <int D, int ROWS, int NW>
 struct TileCopy {
   static constexpr int CPR = D / 8;
   static constexpr int ITER = ROWS * CPR / (64 * NW);
   static_assert(ITER * 64 * NW == ROWS * CPR, "tile must split evenly over the waves");
-  uint32_t off[ITER];  // element offset of this lane's chunk within the tile's rows
-  int wave;
+  uint32_t off[ITER];  // element offset of this lane's chunk from the tile's first row
+  int wave, lane;
+  int64_t rs;
 
-  __device__ __forceinline__ TileCopy(int wave_, int lane) : wave(wave_) {
+  __device__ __forceinline__ TileCopy(int wave_, int lane_, int64_t rs_)
+      : wave(wave_), lane(lane_), rs(rs_) {
 #pragma unroll
     for (int j = 0; j < ITER; ++j) {
       const int s = (j * NW + wave) * 64 + lane;
       const int r = s / CPR, c = (s % CPR) ^ swz<CPR>(r);
-      off[j] = (uint32_t)(r * D + c * 8);
+      off[j] = (uint32_t)(r * rs + c * 8);
     }
   }
 
   __device__ __forceinline__ void operator()(const uint16_t* g, int row0, int nrows,
                                              uint16_t* lds) const {
-    const uint16_t* base = g + (size_t)row0 * D;
-    if (row0 + ROWS <= nrows) {
+    copy_rs(g, rs, row0, nrows, lds);
+  }
+
+  // the same from a matrix of row stride rsm
+  __device__ __forceinline__ void copy_rs(const uint16_t* g, int64_t rsm, int row0, int nrows,
+                                          uint16_t* lds) const {
+    const uint16_t* base = g + (int64_t)row0 * rsm;
+    if (row0 + ROWS <= nrows && rsm == rs) {
 #pragma unroll
       for (int j = 0; j < ITER; ++j)
         __builtin_amdgcn_global_load_lds(base + off[j], lds + (j * NW + wave) * 512, 16, 0, 0);
     } else {
 #pragma unroll
-      for (int j = 0; j < ITER; ++j)
-        __builtin_amdgcn_global_load_lds(base + clamped_chunk_offset(off[j], D, row0, nrows),
+      for (int j = 0; j < ITER; ++j) {
+        const int r = ((j * NW + wave) * 64 + lane) / CPR;
+        const uint32_t o = (uint32_t)((int64_t)off[j] + r * (rsm - rs));  // r * rsm + chunk
+        __builtin_amdgcn_global_load_lds(base + clamped_chunk_offset(o, r, rsm, row0, nrows),
                                          lds + (j * NW + wave) * 512, 16, 0, 0);
+      }
     }
   }
 };

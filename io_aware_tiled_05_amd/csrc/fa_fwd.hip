@@ -53,6 +53,7 @@ struct FwdParams {
   const uint8_t* block_mask;
   int nblk;
   Dropout drop;  // used by the DROP kernels only
+  Strides sq, sk, sv, so;  // element strides of q, k, v, o (lse is packed [B][H][N])
 };
 
 // Compile-time tuning knobs (defaults are the measured best).
@@ -112,11 +113,10 @@ __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(Fwd
   const int npass = kPairs && p.nqt - 1 - rank != rank ? 2 : 1;
   for (int pass = 0; pass < npass; ++pass) {
     const int qt = CAUSAL ? (pass == 0 ? p.nqt - 1 - rank : rank) : rank;
-    const int b = bh / p.H, N = p.N;
-    const size_t base = (size_t)bh * N * D;
-    const uint16_t* Q = p.q + base;
-    const uint16_t* K = p.k + base;
-    const uint16_t* V = p.v + base;
+    const int b = bh / p.H, hd = bh - b * p.H, N = p.N;
+    const uint16_t* Q = p.q + b * p.sq.b + hd * p.sq.h;
+    const uint16_t* K = p.k + b * p.sk.b + hd * p.sk.h;
+    const uint16_t* V = p.v + b * p.sv.b + hd * p.sv.h;
     const int L = valid_keys(p.key_len, b, N);
     const int q0 = qt * BR, qw = q0 + wave * QW;
     const float c = p.c;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(Fwd
       const int row = qw + qb * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        qf[qb][ks] = as_vec8<T>(ldg16(Q + (size_t)row * D + ks * 16 + h * 8, row < N));
+        qf[qb][ks] = as_vec8<T>(ldg16(Q + (int64_t)row * p.sq.n + ks * 16 + h * 8, row < N));
     }
 
     float m[NQB], mc[NQB], l[NQB];  // reference max (raw score), m * c, partial row sum
@@ -282,21 +282,23 @@ __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(Fwd
       }
     };
 
-    const TileCopy<D, kBC, NW> copy(wave, lane);
+    // one set of chunk offsets for K's row stride; V (normally the same
+    // stride) adjusts them when its stride differs
+    const TileCopy<D, kBC, NW> copy(wave, lane, p.sk.n);
 
     // Walk `ntiles` tiles (first key of tile t = key0(t)) with the copy of
     // tile t+1 in flight while tile t is computed.  One barrier per tile.
     auto walk = [&](int ntiles, auto key0) {
       if (ntiles <= 0) return;
       copy(K, key0(0), N, sK0);
-      copy(V, key0(0), N, sV0);
+      copy.copy_rs(V, p.sv.n, key0(0), N, sV0);
       auto step = [&](int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t landed
         __syncthreads();                     // ... and every wave's; tile t-1 fully read
         if (t + 1 < ntiles) {
           const int nk = key0(t + 1);
           copy(K, nk, N, kn);
-          copy(V, nk, N, vn);
+          copy.copy_rs(V, p.sv.n, nk, N, vn);
         }
         compute(kc, vc, key0(t));
       };
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(Fwd
     }
 
     // epilogue: O = O^T / l, lse = (m c + log2 l) ln 2
-    uint16_t* O = p.o + base;
+    uint16_t* O = p.o + b * p.so.b + hd * p.so.h;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const float lt = l[qb] + __shfl_xor(l[qb], 32);
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(Fwd
           for (int i = 0; i < 4; ++i) {
             const f32x4 o4 = {acc[db][qb][4 * i] * inv, acc[db][qb][4 * i + 1] * inv,
                               acc[db][qb][4 * i + 2] * inv, acc[db][qb][4 * i + 3] * inv};
-            *reinterpret_cast<u32x2*>(O + (size_t)query * D + db * 32 + 8 * i + 4 * h) =
+            *reinterpret_cast<u32x2*>(O + (int64_t)query * p.so.n + db * 32 + 8 * i + 4 * h) =
                 pack4<T>(o4);
           }
         if (h == 0)
@@ -371,6 +373,7 @@ struct FwdParamsF32 {
   int period;
   float c;
   const int32_t* key_len;
+  Strides sq, sk, sv, so;
 };
 
 template <int D, bool CAUSAL>
@@ -385,11 +388,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParamsF32 p) {
   int rank, bh;
   map_workgroup(blockIdx.x, p.nqt, p.BH, p.period, &rank, &bh);
   const int qt = CAUSAL ? p.nqt - 1 - rank : rank;
-  const int b = bh / p.H, N = p.N;
-  const size_t base = (size_t)bh * N * D;
-  const float* Q = p.q + base;
-  const float* K = p.k + base;
-  const float* V = p.v + base;
+  const int b = bh / p.H, hd = bh - b * p.H, N = p.N;
+  const float* Q = p.q + b * p.sq.b + hd * p.sq.h;
+  const float* K = p.k + b * p.sk.b + hd * p.sk.h;
+  const float* V = p.v + b * p.sv.b + hd * p.sv.h;
   const int L = valid_keys(p.key_len, b, N);
   const int q0 = qt * kBR, qw = q0 + wave * 32;
 
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParamsF32 p) {
     const int row = qw + qb * 16 + n;
 #pragma unroll
     for (int ks = 0; ks < D / 4; ++ks)
-      qf[qb][ks] = row < N ? Q[(size_t)row * D + ks * 4 + g] : 0.f;
+      qf[qb][ks] = row < N ? Q[(int64_t)row * p.sq.n + ks * 4 + g] : 0.f;
   }
   float m[2] = {neg_inf(), neg_inf()}, l[2] = {0.f, 0.f};
   f32x4 acc[DB][2];
@@ -418,8 +420,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParamsF32 p) {
     __syncthreads();
     for (int c = tid; c < kBC * D; c += 256) {
       const int r = c / D, col = c % D, key = kt0 + r;
-      sK[r * S + col] = key < N ? K[(size_t)key * D + col] : 0.f;
-      sV[r * S + col] = key < N ? V[(size_t)key * D + col] : 0.f;
+      sK[r * S + col] = key < N ? K[(int64_t)key * p.sk.n + col] : 0.f;
+      sV[r * S + col] = key < N ? V[(int64_t)key * p.sv.n + col] : 0.f;
     }
     __syncthreads();
     if (qw >= N || (CAUSAL && kt0 > qw + 31)) continue;
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParamsF32 p) {
             acc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s[kb][qb][i], acc[db][qb], 0, 0, 0);
         }
   }
-  float* O = p.o + base;
+  float* O = p.o + b * p.so.b + hd * p.so.h;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float lt = group_sum(l[qb]);
@@ -495,7 +497,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParamsF32 p) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<f32x4*>(O + (size_t)query * D + db * 16 + g * 4) = acc[db][qb] * inv;
+        *reinterpret_cast<f32x4*>(O + (int64_t)query * p.so.n + db * 16 + g * 4) =
+            acc[db][qb] * inv;
       if (g == 0)
         p.lse[(size_t)bh * N + query] =
             lt > 0.f ? (m[qb] * p.c + fast_log2(lt)) * kLn2 : neg_inf();
@@ -560,6 +563,10 @@ hipError_t launch_fwd_kernel(const FwdArgs& a) {
   p.block_mask = a.block_mask;
   p.nblk = (a.N + 127) / 128;
   p.drop = a.drop;
+  p.sq = a.lay.q;
+  p.sk = a.lay.k;
+  p.sv = a.lay.v;
+  p.so = a.lay.o;
   const int wgs_per_head = CAUSAL && !SPARSE ? (p.nqt + 1) / 2 : p.nqt;
   hipLaunchKernelGGL((fwd_kernel<T, D, NW, QW, CAUSAL, SPARSE, DROP>),
                      dim3(wgs_per_head * p.BH), dim3(64 * NW), 0, a.stream, p);
@@ -603,6 +610,10 @@ hipError_t run_fwd_f32(const FwdArgs& a) {
   p.period = CAUSAL ? snake_period(p.BH) : 0;
   p.c = a.scale * kLog2e;
   p.key_len = a.key_len;
+  p.sq = a.lay.q;
+  p.sk = a.lay.k;
+  p.sv = a.lay.v;
+  p.so = a.lay.o;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(p.nqt * p.BH), dim3(256), 0, a.stream, p);
   return hipGetLastError();
 }

@@ -27,6 +27,24 @@ struct Dropout {
   uint32_t k0 = 0, k1 = 0, offset = 0;
 };
 
+// Element strides of one [B][H][N][d] tensor view: element (b, h, i, c) is
+// at b * b_ + h * h_ + i * n + c (the d index is contiguous).  Packed
+// tensors have n = d, h_ = N d, b_ = H N d.
+struct Strides {
+  int64_t b, h, n;
+};
+inline Strides packed_strides(int64_t H, int64_t N, int64_t d) { return {H * N * d, N * d, d}; }
+
+// Strides of every tensor an entry point touches (those it does not use are
+// ignored).
+struct Layout {
+  Strides q, k, v, o, dO, dq, dk, dv;
+};
+inline Layout packed_layout(int64_t H, int64_t N, int64_t d) {
+  const Strides s = packed_strides(H, N, d);
+  return {s, s, s, s, s, s, s, s};
+}
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -41,6 +59,7 @@ struct FwdArgs {
   int dtype;                 // fa_dtype
   hipStream_t stream;
   Dropout drop = {};
+  Layout lay = {};           // q, k, v, o
 };
 
 struct BwdArgs {
@@ -62,6 +81,7 @@ struct BwdArgs {
   int dtype;
   hipStream_t stream;
   Dropout drop = {};
+  Layout lay = {};           // every tensor; the workspace copies are packed
 };
 
 // Backward workspace, regions 256-byte aligned, in this order:
@@ -102,12 +122,13 @@ inline BwdWorkspace bwd_workspace_layout(int64_t B, int64_t H, int64_t N, int64_
   return w;
 }
 
-// The checks of fa_bwd's arguments (everything but the workspace), made
-// before any HIP call; FA_OK or the status to return.
+// The checks of fa_bwd's arguments (everything but the workspace; the
+// strides when `lay` is given), made before any HIP call; FA_OK or the
+// status to return.
 int bwd_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
               const void* dO, const void* dq, const void* dk, const void* dv, int B, int H,
               int N, int d, float scale, int causal, bool block_sparse, int dtype,
-              bool dropout);
+              bool dropout, const Layout* lay);
 
 // Compute units of the current device (0 if the query fails); cached.
 int device_cu_count();

@@ -59,7 +59,7 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
   // fa_bwd's checks of the caller's arguments, then the scratch limit, all
   // before any HIP call
   const int st = fa::bwd_check(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal,
-                               false, dtype, false);
+                               false, dtype, false, nullptr);
   if (st != FA_OK) return st;
   if (fa_bwd_workspace_size(B, H, N, d) > kScratchBytes) return FA_ERR_TOO_LARGE;
   void* ws = scratch_on_current_device();

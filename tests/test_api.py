@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_dropout", "fa_bwd_noalloc", "fa_bwd_stage",
-        "fa_bwd_workspace_size",
+        "fa_bwd_strided", "fa_bwd_workspace_size", "fa_fwd_strided",
         "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_blocksparse",
         "fa_fwd_dropout", "fa_status_string"])
 
@@ -171,6 +171,70 @@ def test_noalloc_scratch_limit_matches_header(lib):
     # the bench workload's backward fits it, twice its size does not
     assert lib.fa_bwd_workspace_size(1, 16, 16384, 64) <= 128 << 20
     assert lib.fa_bwd_workspace_size(2, 16, 16384, 64) > 128 << 20
+
+
+def strided_layout(d=64, **over):
+    from io_aware_tiled_05_amd._lib import FaLayout, FaStrides
+    N, H = 256, 2
+    packed = dict(batch=H * N * d, head=N * d, row=d)
+    lay = FaLayout(*(FaStrides(**packed) for _ in range(8)))
+    for name, st in over.items():
+        setattr(lay, name, FaStrides(*st))
+    return lay
+
+
+def fwd_strided(lib, lay=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=2, N=256, d=64, scale=0.125, causal=0,
+             key_len=None, bm=None, bs=128, p=0.0, dtype=BF16)
+    a.update(kw)
+    return lib.fa_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                              a["d"], a["scale"], a["causal"], a["key_len"], a["bm"], a["bs"],
+                              a["p"], 1, 0, lay, a["dtype"], None)
+
+
+def bwd_strided(lib, lay=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, dO=P, dq=P, dk=P, dv=P, B=2, H=2, N=256, d=64,
+             scale=0.125, causal=0, key_len=None, bm=None, bs=128, p=0.0, ws=P, ws_bytes=WS,
+             dtype=BF16)
+    a.update(kw)
+    return lib.fa_bwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dO"], a["dq"],
+                              a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                              a["causal"], a["key_len"], a["bm"], a["bs"], a["p"], 1, 0, lay,
+                              a["ws"], a["ws_bytes"], a["dtype"], None)
+
+
+# (layout overrides, other args, forward status, backward status); "ok" means
+# the layout passed validation, shown by the unsupported head dimension 80
+# (checked after the strides) failing next, so that no case reaches a HIP
+# call
+STRIDED_CASES = [
+    (dict(q=(256 * 64, 64, 4)), {}, -1, -1),              # row stride not a multiple of 8
+    (dict(k=(2 * 256 * 64, 64, 2 * 64)), {}, "ok", "ok"),  # [B][N][H][d] views are fine
+    (dict(o=(256 * 64, 64, 32)), {}, -1, "ok"),           # output rows overlap (o is read
+                                                           # only by the backward)
+    (dict(v=(-64, 64, 64)), {}, -1, -1),                  # negative stride
+    (dict(q=(0, 0, 1 << 24)), {}, -1, -1),                # row stride too large
+    (dict(q=(256 * 16, 16, 16)), dict(dtype=F32), "ok", "ok"),  # fp32: multiples of 4
+    (dict(q=(256 * 64, 64, 68)), {}, -1, -1),             # 16-bit: multiples of 8
+    ({}, dict(bm=P, causal=1), -1, -1), ({}, dict(bm=P, p=0.1), -1, -1),
+    ({}, dict(bm=P, bs=64), -2, -2), ({}, dict(p=1.5), -1, -1),
+    ({}, dict(p=0.1, dtype=F32), -2, -2), ({}, dict(bm=P, dtype=F32), -2, -2),
+]
+
+
+@pytest.mark.parametrize("over,kw,fst,bst", STRIDED_CASES)
+def test_strided_validation(lib, over, kw, fst, bst):
+    for call, want in ((fwd_strided, fst), (bwd_strided, bst)):
+        if want == "ok":
+            assert call(lib, strided_layout(d=80, **over), d=80, **kw) == -2
+        else:
+            assert call(lib, strided_layout(**over), **kw) == want
+
+
+def test_strided_output_strides_checked_in_backward(lib):
+    # dq/dk/dv rows must not overlap either (dO, an input, may)
+    for name in ("dq", "dk", "dv"):
+        assert bwd_strided(lib, strided_layout(**{name: (256 * 64, 64, 8)})) == -1
 
 
 @pytest.mark.parametrize("kw,status", [
