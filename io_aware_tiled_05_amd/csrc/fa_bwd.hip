@@ -458,8 +458,8 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
   const uint16_t* const Vin = p.v + b * p.sv.b + hd * p.sv.h;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    u32x4 kr = ldg16(Kin + (int64_t)key * p.sk.n + ks * 16 + h * 8, key < N);
-    u32x4 vr = ldg16(Vin + (int64_t)key * p.sv.n + ks * 16 + h * 8, key < N);
+    u32x4 kr = ldg16_row(Kin, key, p.sk.n, ks * 16 + h * 8, N);
+    u32x4 vr = ldg16_row(Vin, key, p.sv.n, ks * 16 + h * 8, N);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       kr[j] = Elt<TI>::pack2(ldexpf(to_f32<T>(kr[j] & 0xffffu), -ek),
@@ -738,18 +738,18 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
   // convert pass wrote.
   const int kq = -(sc.eo + sc.ev);
   // D of this lane's query (dropout: subtracted after the mask)
-  const float dq_D = DROP && query < N ? p.Dbuf[(size_t)bh * N + query] : 0.f;
+  const float dq_D = DROP ? ldg_f32(p.Dbuf + (size_t)bh * N, query, N, 0.f) : 0.f;
 
   // this wave's queries (c Q 2^-eq, fp16) and output gradients as B
   // operands (lane = query, k = d values)
   hvec8 qf[KS];
   vec8 of[KS];
   const bool qok = query < N;
-  const uint16_t* const dOin = p.dO + b * p.sdO.b + hd * p.sdO.h + (int64_t)query * p.sdO.n;
+  const uint16_t* const dOin = p.dO + b * p.sdO.b + hd * p.sdO.h;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = as_vec8<TI>(ldg16(p.q16 + base + (size_t)query * D + ks * 16 + h * 8, qok));
-    of[ks] = as_vec8<T>(ldg16(dOin + ks * 16 + h * 8, qok));
+    qf[ks] = as_vec8<TI>(ldg16_row(p.q16 + base, query, D, ks * 16 + h * 8, N));
+    of[ks] = as_vec8<T>(ldg16_row(dOin, query, p.sdO.n, ks * 16 + h * 8, N));
   }
   // the row terms of this lane's query (-shift 2^-f for the scores, -D for
   // dP; dropout subtracts D after the mask instead), replicated: every
@@ -761,8 +761,8 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
     // the exponent is m (nsh + S'') when the accumulator is rescaled by m
     // (m = 2^f, or c 2^f in exact mode), else nsh + S''
     const float kqm = sc.mul ? (float)kq / sc.m : (float)kq;
-    const float ns = qok ? p.nsh[(size_t)bh * N + query] + kqm : neg_inf();
-    const float nd = qok && !DROP ? -p.Dbuf[(size_t)bh * N + query] : 0.f;
+    const float ns = ldg_f32(p.nsh + (size_t)bh * N, query, N, neg_inf()) + kqm;
+    const float nd = DROP ? 0.f : -ldg_f32(p.Dbuf + (size_t)bh * N, query, N, 0.f);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       s_init[e] = ns;

@@ -118,10 +118,25 @@ __device__ __forceinline__ f32x4 residual16(f32x4 x) {
   return r;
 }
 
-// 16-byte global load (zero when !valid; the address is not touched then).
-__device__ __forceinline__ u32x4 ldg16(const uint16_t* p, bool valid) {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  return valid ? *reinterpret_cast<const u32x4*>(p) : z;
+// 16 bytes (columns col .. col+7) of row `row` of a tensor with nrows >= 1
+// rows of stride rs elements; zero for row >= nrows.  The load is issued
+// for every lane (from the last row where row >= nrows) and the zero is a
+// select, so a run of these loads is straight-line code: a branch around
+// each load makes the compiler wait for the loads before it at the join,
+// which serialises their latencies in the kernels' prologues.
+__device__ __forceinline__ u32x4 ldg16_row(const uint16_t* base, int row, int64_t rs, int col,
+                                           int nrows) {
+  const int r = row < nrows ? row : nrows - 1;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(base + (int64_t)r * rs + col);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  return row < nrows ? v : z;
+}
+
+// element i of a float array of n >= 1 elements, `other` for i >= n (a
+// select after an unconditional load, as above)
+__device__ __forceinline__ float ldg_f32(const float* a, int i, int n, float other) {
+  const float v = a[i < n ? i : n - 1];
+  return i < n ? v : other;
 }
 
 __device__ __forceinline__ u32x4 lds16(const uint16_t* p) {

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(Fwd
       const int row = qw + qb * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        qf[qb][ks] = as_vec8<T>(ldg16(Q + (int64_t)row * p.sq.n + ks * 16 + h * 8, row < N));
+        qf[qb][ks] = as_vec8<T>(ldg16_row(Q, row, p.sq.n, ks * 16 + h * 8, N));
     }
 
     float m[NQB], mc[NQB], l[NQB];  // reference max (raw score), m * c, partial row sum
