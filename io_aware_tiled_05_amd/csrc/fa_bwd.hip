@@ -338,6 +338,125 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, con
   }
 }
 
+// The D pass of one (b, h) in one workgroup of 1024 threads, for grids of
+// many short heads: the maxima need no second launch (the workgroup
+// reduces them itself), and the second read of Q, K and dO, for the fp16
+// copies, finds them in L2 or the MALL.  Writes exactly what
+// bwd_pre_kernel and bwd_convert_kernel write (the same per-row thread
+// mapping and sum order for D; maxima are order-free), except the partial
+// maxima, which nothing reads on this path.  Rows are staged in LDS only
+// as D and shift (2 N floats, N <= kHeadPrepMaxN).
+constexpr int kHeadPrepMaxN = 2048;
+template <typename T, int D>
+__global__ __launch_bounds__(1024) void bwd_prep_head_kernel(
+    const uint16_t* o, const uint16_t* dO, const float* lse, const uint16_t* q,
+    const uint16_t* k, const uint16_t* v, float* Dbuf, float* shift, uint32_t* maxes, float c,
+    uint16_t* q16, uint16_t* k16, uint16_t* do16, float* nDs, float* nsh, int N, int BH,
+    int rexp, int H, Layout lay) {
+  constexpr int TPR = pre_tpr<D>();  // threads per row for D, as bwd_pre_kernel
+  constexpr int RPB = 1024 / TPR;
+  __shared__ float sD[kHeadPrepMaxN], sS[kHeadPrepMaxN];
+  __shared__ uint32_t red[4][16];
+  const int bh = blockIdx.x;
+  const int b = bh / H, hd = bh - b * H;
+  o += b * lay.o.b + hd * lay.o.h;
+  dO += b * lay.dO.b + hd * lay.dO.h;
+  q += b * lay.q.b + hd * lay.q.h;
+  k += b * lay.k.b + hd * lay.k.h;
+  v += b * lay.v.b + hd * lay.v.h;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  {
+    const int c8 = (tid % TPR) * 8;
+    const bool col_ok = c8 < D;
+    uint32_t mx[4] = {0u, 0u, 0u, 0u};
+    for (int r0 = 0; r0 < N; r0 += RPB) {
+      const int r = r0 + tid / TPR;
+      const bool ok = r < N;
+      float s = 0.f;
+      if (ok && col_ok) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(o + r * lay.o.n + c8);
+        const u32x4 g = *reinterpret_cast<const u32x4*>(dO + r * lay.dO.n + c8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s = fmaf(to_f32<T>(a[j] & 0xffffu), to_f32<T>(g[j] & 0xffffu), s);
+          s = fmaf(to_f32<T>(a[j] >> 16), to_f32<T>(g[j] >> 16), s);
+        }
+        const uint32_t m0 = absmax8<T>(*reinterpret_cast<const u32x4*>(q + r * lay.q.n + c8));
+        const uint32_t m1 = absmax8<T>(*reinterpret_cast<const u32x4*>(k + r * lay.k.n + c8));
+        const uint32_t m2 = absmax8<T>(*reinterpret_cast<const u32x4*>(v + r * lay.v.n + c8));
+        const uint32_t m3 = absmax8<T>(g);
+        mx[0] = mx[0] > m0 ? mx[0] : m0;
+        mx[1] = mx[1] > m1 ? mx[1] : m1;
+        mx[2] = mx[2] > m2 ? mx[2] : m2;
+        mx[3] = mx[3] > m3 ? mx[3] : m3;
+      }
+#pragma unroll
+      for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      if (ok && c8 == 0) {
+        const int64_t row = (int64_t)bh * N + r;
+        const float l = lse[row];
+        const float sh = l == neg_inf() ? pos_inf() : l * kLog2e;
+        Dbuf[row] = s;
+        shift[row] = sh;
+        sD[r] = s;
+        sS[r] = sh;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t o2 = (uint32_t)__shfl_xor((int)mx[t], off);
+        mx[t] = mx[t] > o2 ? mx[t] : o2;
+      }
+    if (lane == 0)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) red[t][wave] = mx[t];
+  }
+  __syncthreads();
+  uint32_t mx[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    uint32_t m = red[t][0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) m = m > red[t][w] ? m : red[t][w];
+    mx[t] = m;
+  }
+  if (tid == 0)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) maxes[(size_t)t * BH + bh] = mx[t];
+  const Scales sc = bwd_scales_of<D>(mx[0], mx[1], mx[2], mx[3], c);
+  // the fp16 copies and row terms, as bwd_convert_kernel
+  constexpr int CT = D / 8;      // threads per row, 16 bytes each
+  constexpr int CR = 1024 / CT;  // rows per pass (d = 96: 85, 4 threads idle)
+  if (tid >= CR * CT) return;
+  const int col = (tid % CT) * 8;
+  const float cq = ldexpf(sc.exact ? 1.f : c, -sc.eq);
+  for (int r = tid / CT; r < N; r += CR) {
+    const int64_t row = (int64_t)bh * N + r;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(q + r * lay.q.n + col);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + r * lay.dO.n + col);
+    const u32x4 kk = *reinterpret_cast<const u32x4*>(k + r * lay.k.n + col);
+    u32x4 ra, rg, rk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ra[j] = Elt<_Float16>::pack2(cq * to_f32<T>(a[j] & 0xffffu), cq * to_f32<T>(a[j] >> 16));
+      rg[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(g[j] & 0xffffu), -sc.eo),
+                                   ldexpf(to_f32<T>(g[j] >> 16), -sc.eo));
+      rk[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(kk[j] & 0xffffu), -sc.ek),
+                                   ldexpf(to_f32<T>(kk[j] >> 16), -sc.ek));
+    }
+    *reinterpret_cast<u32x4*>(q16 + row * D + col) = ra;
+    *reinterpret_cast<u32x4*>(do16 + row * D + col) = rg;
+    *reinterpret_cast<u32x4*>(k16 + row * D + col) = rk;
+    if (col == 0) {
+      nDs[row] = -ldexpf(sD[r], -(sc.eo + sc.ev));
+      const float sh = sS[r] + (float)rexp;
+      nsh[row] = sc.exact ? -sh / sc.m : -ldexpf(sh, -sc.f);
+    }
+  }
+}
+
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -985,6 +1104,10 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_fused_kernel(BwdPara
   template __global__ void bwd_fused_kernel<T, D, true, false, true>(BwdParams);   \
   template __global__ void bwd_fused_kernel<T, D, false, false, true>(BwdParams);  \
   template __global__ void bwd_fused_kernel<T, D, false, true, false>(BwdParams);  \
+  template __global__ void bwd_prep_head_kernel<T, D>(                             \
+      const uint16_t*, const uint16_t*, const float*, const uint16_t*, const uint16_t*, \
+      const uint16_t*, float*, float*, uint32_t*, float, uint16_t*, uint16_t*, uint16_t*, \
+      float*, float*, int, int, int, int, Layout);                                 \
   template __global__ void bwd_convert_kernel<T, D>(                               \
       const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*,   \
       const uint32_t*, int, uint32_t*, float,                                        \
@@ -998,6 +1121,14 @@ FA_BWD_INSTANTIATE(_Float16, 64)
 FA_BWD_INSTANTIATE(_Float16, 96)
 FA_BWD_INSTANTIATE(_Float16, 128)
 #undef FA_BWD_INSTANTIATE
+
+// The D pass in one launch (one workgroup per head) when there are enough
+// heads to spread over the GPU and each is short; otherwise the two
+// launches whose grids split every head over many workgroups.  Measured
+// (stage D alone, bf16): 61 -> 56 us at B = 16, H = 16, N = 1024; 29 -> 26 us
+// at 8 x 12 x 1024; 67 -> 63 us at 8 x 16 x 2048; 26 -> 25 us at 2 x 16 x 1024;
+// but 60 -> 94 us at 4 x 16 x 4096 (too few workgroups for the bytes).
+inline bool head_prep(int N, int BH) { return N <= kHeadPrepMaxN && BH >= 32; }
 
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t run_bwd(const BwdArgs& a, int stage) {
@@ -1017,7 +1148,15 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   uint16_t* k16 = reinterpret_cast<uint16_t*>(ws + w.k16);
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   const uint16_t* dO = static_cast<const uint16_t*>(a.dO);
-  if (stage == 0 || stage == 1) {
+  if ((stage == 0 || stage == 1) && head_prep(a.N, BH)) {
+    hipLaunchKernelGGL((bwd_prep_head_kernel<T, D>), dim3(BH), dim3(1024), 0, a.stream,
+                       static_cast<const uint16_t*>(a.o), dO, a.lse, q,
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), Dbuf,
+                       shift, maxes, c, q16, k16, do16, nDs, nsh, a.N, BH,
+                       a.drop.on ? a.drop.rexp : 0, a.H, a.lay);
+    e = hipGetLastError();
+    if (e != hipSuccess || stage == 1) return e;
+  } else if (stage == 0 || stage == 1) {
     // row groups per workgroup of the D pass: enough for a grid of about
     // 2048 workgroups, and at least enough that a head has at most
     // kPreChunks workgroups (one partial maximum each)

@@ -89,3 +89,34 @@ def test_stages_against_oracle(fa):
     print("[bwd stages vs oracle bf16 d=64 N=300 causal]")
     for name, got, want in zip(("dq", "dk", "dv"), staged, ref):
         assert_close(name, to_np(got), want, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("N,mask", [(300, "causal"), (1024, "none"), (2048, "causal"),
+                                    (517, "dropout")])
+def test_one_launch_d_pass_equals_split(fa, dtype, d, N, mask):
+    """With 32 or more heads of at most 2048 rows the D pass runs as one
+    workgroup per head; otherwise as two launches over many workgroups per
+    head.  Both write the same D, shift, maxima, fp16 copies and row terms,
+    so the gradients of the first heads of a 32-head call must equal, bit
+    for bit, those of a 4-head call holding only them (b = 0, so every head
+    keeps its index, which the dropout draw depends on)."""
+    import torch
+    x = make_inputs(Workload("headprep", 1, 32, N, d, dtype, seed=71))
+    q, k, v, dO = (to_dev(x[n], dtype) for n in ("q", "k", "v", "dO"))
+    s = x["scale"]
+    print(f"[one-launch D pass {dtype} d={d} N={N} {mask}]", flush=True)
+
+    def grads(q, k, v, dO):
+        if mask == "dropout":
+            o, lse = fa.fa_fwd_dropout(q, k, v, 0.2, 99, 3, scale=s, causal=True)
+            return fa.fa_bwd_dropout(q, k, v, o, lse, dO, 0.2, 99, 3, scale=s, causal=True)
+        o, lse = fa.fa_fwd(q, k, v, scale=s, causal=mask == "causal")
+        return fa.fa_bwd(q, k, v, o, lse, dO, scale=s, causal=mask == "causal")
+
+    full = grads(q, k, v, dO)
+    part = grads(*(t[:, :4].contiguous() for t in (q, k, v, dO)))
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), full, part):
+        assert torch.equal(a[:, :4], b), f"{name}: one-launch and split D passes differ"
