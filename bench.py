@@ -417,9 +417,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # about 100 ms of work at the default workload: with 5 warm-up steps
-    # (12 ms) the first timed loop still ran about 3 % slow
-    ap.add_argument("--warmup", type=int, default=40)
+    # about 250 ms of work at the default workload: with 5 warm-up steps
+    # (12 ms) the first timed loop still ran about 3 % slow, with 40 about
+    # 1 % slower than with 200
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="long_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV",
