@@ -154,6 +154,24 @@ __device__ __forceinline__ Scales bwd_scales(const uint32_t* maxes, int BH, int 
   return bwd_scales_of<D>(maxes[bh], maxes[BH + bh], maxes[2 * BH + bh], maxes[3 * BH + bh], c);
 }
 
+// The raw path's scales: Q and K enter the products unscaled (in the
+// input type, exactly), so c multiplies the score accumulator in fp32
+// (exact mode, m = c, f = 0); dO and V keep their power-of-two scales (the
+// fp16 copy of dO, V converted in registers), from their maxima alone.
+__device__ __forceinline__ Scales raw_scales_of(uint32_t mxv, uint32_t mxo, float c) {
+  Scales s;
+  s.eq = s.ek = s.f = 0;
+  s.ev = scale_exp(mxv, kTv);
+  s.eo = scale_exp(mxo, kTo);
+  s.exact = true;
+  s.mul = true;
+  s.m = c;
+  return s;
+}
+__device__ __forceinline__ Scales bwd_raw_scales(const uint32_t* maxes, int BH, int bh, float c) {
+  return raw_scales_of(maxes[2 * BH + bh], maxes[3 * BH + bh], c);
+}
+
 // largest |x| of the 8 16-bit values in a 16-byte chunk, as float bits
 // (magnitude bit patterns of both formats order like the values)
 template <typename T>
@@ -185,7 +203,7 @@ constexpr int pre_tpr() {
   return D / 8 <= 4 ? 4 : D / 8 <= 8 ? 8 : 16;
 }
 
-template <typename T, int D, bool STATS>
+template <typename T, int D, bool STATS, bool RAW>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const uint16_t* dO,
                                                       const float* lse, const uint16_t* q,
                                                       const uint16_t* k, const uint16_t* v,
@@ -220,8 +238,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
         s = fmaf(to_f32<T>(a[j] >> 16), to_f32<T>(g[j] >> 16), s);
       }
       if (STATS) {
-        const uint32_t m0 = absmax8<T>(*reinterpret_cast<const u32x4*>(q + r * lay.q.n + c));
-        const uint32_t m1 = absmax8<T>(*reinterpret_cast<const u32x4*>(k + r * lay.k.n + c));
+        // the raw path scales neither Q nor K: their maxima stay 0
+        const uint32_t m0 =
+            RAW ? 0u : absmax8<T>(*reinterpret_cast<const u32x4*>(q + r * lay.q.n + c));
+        const uint32_t m1 =
+            RAW ? 0u : absmax8<T>(*reinterpret_cast<const u32x4*>(k + r * lay.k.n + c));
         const uint32_t m2 = absmax8<T>(*reinterpret_cast<const u32x4*>(v + r * lay.v.n + c));
         const uint32_t m3 = absmax8<T>(g);
         mx[0] = mx[0] > m0 ? mx[0] : m0;
@@ -269,7 +290,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* o, const u
 // the head's nchunk partial maxima from the D pass itself (iters > 1 on
 // large grids spreads that over more rows); the head's first workgroup
 // also stores them in maxes[4][BH] for the dK/dV and dQ kernels.
-template <typename T, int D>
+template <typename T, int D, bool RAW>
 __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, const uint16_t* k,
                                                           const uint16_t* dO, const float* Dbuf,
                                                           const float* shift,
@@ -306,7 +327,8 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, con
 #pragma unroll
     for (int t = 0; t < 4; ++t) maxes[(size_t)t * BH + bh] = mx[t];
   }
-  const Scales sc = bwd_scales_of<D>(mx[0], mx[1], mx[2], mx[3], c);
+  const Scales sc = RAW ? raw_scales_of(mx[2], mx[3], c)
+                        : bwd_scales_of<D>(mx[0], mx[1], mx[2], mx[3], c);
   if ((int)threadIdx.x >= RPB * TPR) return;
   const int col = (int)(threadIdx.x % TPR) * 8;
   const float cq = ldexpf(sc.exact ? 1.f : c, -sc.eq);
@@ -314,21 +336,27 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, con
     const int r = (rb * iters + it) * RPB + (int)(threadIdx.x / TPR);
     if (r >= N) return;
     const int64_t row = (int64_t)bh * N + r;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(q + r * lay.q.n + col);
     const u32x4 g = *reinterpret_cast<const u32x4*>(dO + r * lay.dO.n + col);
-    const u32x4 kk = *reinterpret_cast<const u32x4*>(k + r * lay.k.n + col);
-    u32x4 ra, rg, rk;
+    u32x4 rg;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ra[j] = Elt<_Float16>::pack2(cq * to_f32<T>(a[j] & 0xffffu), cq * to_f32<T>(a[j] >> 16));
+    for (int j = 0; j < 4; ++j)
       rg[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(g[j] & 0xffffu), -sc.eo),
                                    ldexpf(to_f32<T>(g[j] >> 16), -sc.eo));
-      rk[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(kk[j] & 0xffffu), -sc.ek),
-                                   ldexpf(to_f32<T>(kk[j] >> 16), -sc.ek));
-    }
-    *reinterpret_cast<u32x4*>(q16 + row * D + col) = ra;
     *reinterpret_cast<u32x4*>(do16 + row * D + col) = rg;
-    *reinterpret_cast<u32x4*>(k16 + row * D + col) = rk;
+    if constexpr (!RAW) {  // the raw path reads Q and K themselves
+      const u32x4 a = *reinterpret_cast<const u32x4*>(q + r * lay.q.n + col);
+      const u32x4 kk = *reinterpret_cast<const u32x4*>(k + r * lay.k.n + col);
+      u32x4 ra, rk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ra[j] = Elt<_Float16>::pack2(cq * to_f32<T>(a[j] & 0xffffu),
+                                     cq * to_f32<T>(a[j] >> 16));
+        rk[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(kk[j] & 0xffffu), -sc.ek),
+                                     ldexpf(to_f32<T>(kk[j] >> 16), -sc.ek));
+      }
+      *reinterpret_cast<u32x4*>(q16 + row * D + col) = ra;
+      *reinterpret_cast<u32x4*>(k16 + row * D + col) = rk;
+    }
     if (col == 0) {
       nDs[row] = -ldexpf(Dbuf[row], -(sc.eo + sc.ev));
       // with dropout the exponent also carries -rexp: P 2^-rexp (see Dropout)
@@ -347,7 +375,7 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const uint16_t* q, con
 // maxima, which nothing reads on this path.  Rows are staged in LDS only
 // as D and shift (2 N floats, N <= kHeadPrepMaxN).
 constexpr int kHeadPrepMaxN = 2048;
-template <typename T, int D>
+template <typename T, int D, bool RAW>
 __global__ __launch_bounds__(1024) void bwd_prep_head_kernel(
     const uint16_t* o, const uint16_t* dO, const float* lse, const uint16_t* q,
     const uint16_t* k, const uint16_t* v, float* Dbuf, float* shift, uint32_t* maxes, float c,
@@ -381,8 +409,10 @@ __global__ __launch_bounds__(1024) void bwd_prep_head_kernel(
           s = fmaf(to_f32<T>(a[j] & 0xffffu), to_f32<T>(g[j] & 0xffffu), s);
           s = fmaf(to_f32<T>(a[j] >> 16), to_f32<T>(g[j] >> 16), s);
         }
-        const uint32_t m0 = absmax8<T>(*reinterpret_cast<const u32x4*>(q + r * lay.q.n + c8));
-        const uint32_t m1 = absmax8<T>(*reinterpret_cast<const u32x4*>(k + r * lay.k.n + c8));
+        const uint32_t m0 =
+            RAW ? 0u : absmax8<T>(*reinterpret_cast<const u32x4*>(q + r * lay.q.n + c8));
+        const uint32_t m1 =
+            RAW ? 0u : absmax8<T>(*reinterpret_cast<const u32x4*>(k + r * lay.k.n + c8));
         const uint32_t m2 = absmax8<T>(*reinterpret_cast<const u32x4*>(v + r * lay.v.n + c8));
         const uint32_t m3 = absmax8<T>(g);
         mx[0] = mx[0] > m0 ? mx[0] : m0;
@@ -425,7 +455,8 @@ __global__ __launch_bounds__(1024) void bwd_prep_head_kernel(
   if (tid == 0)
 #pragma unroll
     for (int t = 0; t < 4; ++t) maxes[(size_t)t * BH + bh] = mx[t];
-  const Scales sc = bwd_scales_of<D>(mx[0], mx[1], mx[2], mx[3], c);
+  const Scales sc = RAW ? raw_scales_of(mx[2], mx[3], c)
+                        : bwd_scales_of<D>(mx[0], mx[1], mx[2], mx[3], c);
   // the fp16 copies and row terms, as bwd_convert_kernel
   constexpr int CT = D / 8;      // threads per row, 16 bytes each
   constexpr int CR = 1024 / CT;  // rows per pass (d = 96: 85, 4 threads idle)
@@ -434,21 +465,27 @@ __global__ __launch_bounds__(1024) void bwd_prep_head_kernel(
   const float cq = ldexpf(sc.exact ? 1.f : c, -sc.eq);
   for (int r = tid / CT; r < N; r += CR) {
     const int64_t row = (int64_t)bh * N + r;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(q + r * lay.q.n + col);
     const u32x4 g = *reinterpret_cast<const u32x4*>(dO + r * lay.dO.n + col);
-    const u32x4 kk = *reinterpret_cast<const u32x4*>(k + r * lay.k.n + col);
-    u32x4 ra, rg, rk;
+    u32x4 rg;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ra[j] = Elt<_Float16>::pack2(cq * to_f32<T>(a[j] & 0xffffu), cq * to_f32<T>(a[j] >> 16));
+    for (int j = 0; j < 4; ++j)
       rg[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(g[j] & 0xffffu), -sc.eo),
                                    ldexpf(to_f32<T>(g[j] >> 16), -sc.eo));
-      rk[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(kk[j] & 0xffffu), -sc.ek),
-                                   ldexpf(to_f32<T>(kk[j] >> 16), -sc.ek));
-    }
-    *reinterpret_cast<u32x4*>(q16 + row * D + col) = ra;
     *reinterpret_cast<u32x4*>(do16 + row * D + col) = rg;
-    *reinterpret_cast<u32x4*>(k16 + row * D + col) = rk;
+    if constexpr (!RAW) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(q + r * lay.q.n + col);
+      const u32x4 kk = *reinterpret_cast<const u32x4*>(k + r * lay.k.n + col);
+      u32x4 ra, rk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ra[j] = Elt<_Float16>::pack2(cq * to_f32<T>(a[j] & 0xffffu),
+                                     cq * to_f32<T>(a[j] >> 16));
+        rk[j] = Elt<_Float16>::pack2(ldexpf(to_f32<T>(kk[j] & 0xffffu), -sc.ek),
+                                     ldexpf(to_f32<T>(kk[j] >> 16), -sc.ek));
+      }
+      *reinterpret_cast<u32x4*>(q16 + row * D + col) = ra;
+      *reinterpret_cast<u32x4*>(k16 + row * D + col) = rk;
+    }
     if (col == 0) {
       nDs[row] = -ldexpf(sD[r], -(sc.eo + sc.ev));
       const float sh = sS[r] + (float)rexp;
@@ -456,6 +493,9 @@ __global__ __launch_bounds__(1024) void bwd_prep_head_kernel(
     }
   }
 }
+
+template <bool R, typename A, typename B> struct Pick { typedef B type; };
+template <typename A, typename B> struct Pick<true, A, B> { typedef A type; };
 
 struct BwdParams {
   const uint16_t* q;
@@ -482,9 +522,11 @@ struct BwdParams {
   const int32_t* key_len;
   const uint8_t* block_mask;
   int nblk;
-  // element strides of the caller's k, v, dO, dq, dk, dv (q, o are read
-  // only by the D pass; the workspace copies are packed [BH][N][d])
+  // element strides of the caller's k, v, dO, dq, dk, dv and q (q and o are
+  // read only by the D pass, except by the raw path; the workspace copies
+  // are packed [BH][N][d])
   Strides sk, sv, sdO, sdq, sdk, sdv;
+  Strides sq;  // the raw path reads Q in the gradient kernels too
 };
 
 // B operand (P or dS, 16 keys or queries of chunk a) from a 32x32
@@ -539,10 +581,14 @@ struct DkdvLds {
 };
 
 // workgroup `wg` of the dK/dV grid
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool RAW>
 __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SPARSE>& lds) {
   constexpr int KS = D / 16, DB = D / 32, TILE = kBQ * D, NW = 4;
+  // operand types: TQ for Q, K and dS (S = Q K^T, dK = dS^T Q), fp16 for dO,
+  // V and P (dP = dO V^T, dV = P^T dO)
+  typedef typename Pick<RAW, T, _Float16>::type TQ;
   typedef _Float16 TI;
+  typedef typename Elt<TQ>::vec8 qvec8;
   typedef typename Elt<TI>::vec8 vec8;
   uint16_t* const sQ0 = lds.q0;
   uint16_t* const sQ1 = lds.q1;
@@ -562,17 +608,22 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
   const int kt = rank;  // causal: the lowest key tiles see the most queries, so go first
   const int b = bh / p.H, hd = bh - b * p.H, N = p.N;
   const size_t base = (size_t)bh * N * D;  // the packed workspace copies
-  const uint16_t* Q = p.q16 + base;    // c Q 2^-eq
-  const uint16_t* dO = p.do16 + base;  // dO 2^-eo
+  // Q (raw) or c Q 2^-eq (fp16 copy); dO 2^-eo (fp16 copy)
+  const uint16_t* Q = RAW ? p.q + b * p.sq.b + hd * p.sq.h : p.q16 + base;
+  const uint16_t* dO = p.do16 + base;
+  const int64_t qrs = RAW ? p.sq.n : D;  // Q's row stride (the copies are packed)
   const float* nsh = p.nsh + (size_t)bh * N;
   const float* nD = p.nDs + (size_t)bh * N;
   const int L = valid_keys(p.key_len, b, N);
   const int k0 = kt * kBKV, kw = k0 + wave * 32, key = kw + l32;
-  const Scales sc = bwd_scales<D>(p.maxes, p.BH, bh, p.c);
+  const Scales sc =
+      RAW ? bwd_raw_scales(p.maxes, p.BH, bh, p.c) : bwd_scales<D>(p.maxes, p.BH, bh, p.c);
   const int ek = sc.ek, ev = sc.ev;
 
-  // this wave's keys and values as B operands (lane = key, k = d values)
-  vec8 kf[KS], vf[KS];
+  // this wave's keys (K, or K 2^-ek in fp16) and values (V 2^-ev, fp16) as
+  // B operands (lane = key, k = d values)
+  qvec8 kf[KS];
+  vec8 vf[KS];
   const uint16_t* const Kin = p.k + b * p.sk.b + hd * p.sk.h;
   const uint16_t* const Vin = p.v + b * p.sv.b + hd * p.sv.h;
 #pragma unroll
@@ -581,12 +632,13 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
     u32x4 vr = ldg16_row(Vin, key, p.sv.n, ks * 16 + h * 8, N);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      kr[j] = Elt<TI>::pack2(ldexpf(to_f32<T>(kr[j] & 0xffffu), -ek),
-                             ldexpf(to_f32<T>(kr[j] >> 16), -ek));
+      if constexpr (!RAW)
+        kr[j] = Elt<TI>::pack2(ldexpf(to_f32<T>(kr[j] & 0xffffu), -ek),
+                               ldexpf(to_f32<T>(kr[j] >> 16), -ek));
       vr[j] = Elt<TI>::pack2(ldexpf(to_f32<T>(vr[j] & 0xffffu), -ev),
                              ldexpf(to_f32<T>(vr[j] >> 16), -ev));
     }
-    kf[ks] = as_vec8<TI>(kr);
+    kf[ks] = as_vec8<TQ>(kr);
     vf[ks] = as_vec8<TI>(vr);
   }
   f32x16 dk[DB], dv[DB];  // dK^T, dV^T: rows d = 32db + 8i + 4h + j, column = key
@@ -605,7 +657,7 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
     for (int db = 0; db < DB; ++db)
       toff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec, db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
 
-  const TileCopy<D, kBQ, NW> copy(wave, lane, D);  // the packed copies of Q and dO
+  const TileCopy<D, kBQ, NW> copy(wave, lane, qrs);  // Q; dO's tiles adjust to its stride
   const bool any_key = kw < L;  // every key of this wave padded away -> zero gradients
 
   auto compute = [&](const uint16_t* tq, const uint16_t* to, const float* tl, const float* td,
@@ -633,9 +685,9 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const vec8 aq = as_vec8<TI>(lds16(tq + roff[ks] + qb * 32 * D));
+        const qvec8 aq = as_vec8<TQ>(lds16(tq + roff[ks] + qb * 32 * D));
         const vec8 ao = as_vec8<TI>(lds16(to + roff[ks] + qb * 32 * D));
-        s[qb] = Elt<TI>::mfma32(aq, kf[ks], s[qb]);
+        s[qb] = Elt<TQ>::mfma32(aq, kf[ks], s[qb]);
         dp[qb] = Elt<TI>::mfma32(ao, vf[ks], dp[qb]);
       }
     // P = exp2(c s - shift_row), dS' = P (dP - D_row) 2^-(eo+ev)
@@ -720,15 +772,15 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
 #pragma unroll
     for (int a = 0; a < kBQ / 16; ++a) {
       const vec8 pb = pack_chunk<TI>(s[a >> 1], a & 1);
-      const vec8 sb = pack_chunk<TI>(dp[a >> 1], a & 1);
+      const qvec8 sb = pack_chunk<TQ>(dp[a >> 1], a & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const vec8 ao = join8<TI>(lds_tr4(to + toff[0][db] + a * 16 * D),
                                   lds_tr4(to + toff[1][db] + a * 16 * D));
-        const vec8 aq = join8<TI>(lds_tr4(tq + toff[0][db] + a * 16 * D),
-                                  lds_tr4(tq + toff[1][db] + a * 16 * D));
+        const qvec8 aq = join8<TQ>(lds_tr4(tq + toff[0][db] + a * 16 * D),
+                                   lds_tr4(tq + toff[1][db] + a * 16 * D));
         dv[db] = Elt<TI>::mfma32(ao, pb, dv[db]);
-        dk[db] = Elt<TI>::mfma32(aq, sb, dk[db]);
+        dk[db] = Elt<TQ>::mfma32(aq, sb, dk[db]);
       }
     }
   };
@@ -739,7 +791,7 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
     auto load = [&](int r0, uint16_t* dq_, uint16_t* do_, float* dl, float* dd)
         __attribute__((always_inline)) {
       copy(Q, r0, N, dq_);
-      copy(dO, r0, N, do_);
+      copy.copy_rs(dO, D, r0, N, do_);
       if (wave == 0) copy_row_stat(nsh, r0, N, dl, lane);
       if (wave == 1) copy_row_stat(nD, r0, N, dd, lane);
     };
@@ -821,10 +873,10 @@ struct DqLds {
 };
 
 // workgroup `wg` of the dQ grid
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool RAW>
 __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE>& lds) {
   constexpr int KS = D / 16, DB = D / 32, TILE = kBC * D, NW = 4;
-  typedef _Float16 TI;
+  typedef typename Pick<RAW, T, _Float16>::type TI;  // the score and dQ operand type
   typedef typename Elt<TI>::vec8 hvec8;
   typedef typename Elt<T>::vec8 vec8;
   uint16_t* const sK0 = lds.k0;
@@ -841,12 +893,15 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
   const int qt = CAUSAL ? p.ntiles - 1 - rank : rank;  // longest rows first
   const int b = bh / p.H, hd = bh - b * p.H, N = p.N;
   const size_t base = (size_t)bh * N * D;  // the packed workspace copies
-  const uint16_t* K = p.k16 + base;  // K 2^-ek, fp16
+  // K 2^-ek (fp16 copy) or K itself (raw)
+  const uint16_t* K = RAW ? p.k + b * p.sk.b + hd * p.sk.h : p.k16 + base;
+  const int64_t krs = RAW ? p.sk.n : D;  // its row stride
   const uint16_t* V = p.v + b * p.sv.b + hd * p.sv.h;
   const int L = valid_keys(p.key_len, b, N);
   const int q0 = qt * kBR, qw = q0 + wave * 32, query = qw + l32;
-  const Scales sc = bwd_scales<D>(p.maxes, p.BH, bh, p.c);
-  // dS is rounded to fp16 for dQ = dS K.  dP and D here are unscaled (raw
+  const Scales sc =
+      RAW ? bwd_raw_scales(p.maxes, p.BH, bh, p.c) : bwd_scales<D>(p.maxes, p.BH, bh, p.c);
+  // dS is rounded to fp16 (raw path: the input type) for dQ = dS K.  dP and D here are unscaled (raw
   // dO against raw V), so P carries the power of two 2^kq, kq = -(eo + ev),
   // that the dK/dV kernel's dS gets from its scaled dO and V copies: then
   // |dS'| = |P 2^kq (dP - D)| <= 2 d max|dO'| max|V'| < 2^15 for d <= 128,
@@ -867,7 +922,9 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
   const uint16_t* const dOin = p.dO + b * p.sdO.b + hd * p.sdO.h;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = as_vec8<TI>(ldg16_row(p.q16 + base, query, D, ks * 16 + h * 8, N));
+    qf[ks] = as_vec8<TI>(RAW ? ldg16_row(p.q + b * p.sq.b + hd * p.sq.h, query, p.sq.n,
+                                         ks * 16 + h * 8, N)
+                             : ldg16_row(p.q16 + base, query, D, ks * 16 + h * 8, N));
     of[ks] = as_vec8<T>(ldg16_row(dOin, query, p.sdO.n, ks * 16 + h * 8, N));
   }
   // the row terms of this lane's query (-shift 2^-f for the scores, -D for
@@ -904,9 +961,9 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
     for (int db = 0; db < DB; ++db)
       toff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec, db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
 
-  // chunk offsets for the packed K copy; V's tiles adjust them when its
-  // row stride is not d
-  const TileCopy<D, kBC, NW> copy(wave, lane, D);
+  // chunk offsets for K's tiles; V's tiles adjust them when its row stride
+  // differs
+  const TileCopy<D, kBC, NW> copy(wave, lane, krs);
 
   // `prefetch` starts the copies of the next tile; it runs inside the
   // compute, after the score products are issued, so that the copies (which
@@ -1052,16 +1109,16 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
 }
 
 // The two gradient kernels as separate launches (fa_bwd_stage) ...
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool RAW>
 __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ DkdvLds<D, SPARSE> lds;
-  bwd_dkdv_body<T, D, CAUSAL, SPARSE, DROP>(p, (int)blockIdx.x, lds);
+  bwd_dkdv_body<T, D, CAUSAL, SPARSE, DROP, RAW>(p, (int)blockIdx.x, lds);
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool RAW>
 __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams p) {
   __shared__ DqLds<D, SPARSE> lds;
-  bwd_dq_body<T, D, CAUSAL, SPARSE, DROP>(p, (int)blockIdx.x, lds);
+  bwd_dq_body<T, D, CAUSAL, SPARSE, DROP, RAW>(p, (int)blockIdx.x, lds);
 }
 
 // ... and as one launch (fa_bwd): the dK/dV and dQ kernels need only what
@@ -1069,7 +1126,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dq_kernel(BwdParams 
 // take dK/dV and the rest dQ, and dQ workgroups start while the last,
 // longest dK/dV workgroups still run (short sequences leave most compute
 // units idle in each kernel's tail).  The two LDS layouts share one buffer.
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool RAW>
 __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_fused_kernel(BwdParams p) {
   static_assert(kBKV == kBR, "one tile count for both parts of the grid");
   __shared__ union {
@@ -1078,40 +1135,57 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_fused_kernel(BwdPara
   } lds;
   const int n = p.ntiles * p.BH;
   if ((int)blockIdx.x < n)
-    bwd_dkdv_body<T, D, CAUSAL, SPARSE, DROP>(p, (int)blockIdx.x, lds.kv);
+    bwd_dkdv_body<T, D, CAUSAL, SPARSE, DROP, RAW>(p, (int)blockIdx.x, lds.kv);
   else
-    bwd_dq_body<T, D, CAUSAL, SPARSE, DROP>(p, (int)blockIdx.x - n, lds.q);
+    bwd_dq_body<T, D, CAUSAL, SPARSE, DROP, RAW>(p, (int)blockIdx.x - n, lds.q);
+}
+
+// fp16 inputs take the raw path: Q and K enter the gradient products as
+// they are (exact fp16 products, c applied to the score accumulator in
+// fp32), so the D pass needs neither their maxima nor their copies (about
+// half its bytes); dS stays fp16 with its power-of-two scale, as on the
+// scaled path.  bf16 inputs keep the scaled fp16 copies: their raw
+// products would need dS in bf16 for dK = dS^T Q, whose 8 bits cost dK
+// up to 2.4e-2 against the oracle on a head with 17 unpadded keys
+// (1.4e-2 with fp16 dS), past the bf16 gate.
+template <typename T>
+constexpr bool use_raw() {
+  return !kIsBf16<T>;
 }
 
 // Every kernel the launcher below can select (the host pass of this compiler
 // otherwise leaves some kernel-template launch stubs undefined).
-#define FA_BWD_INSTANTIATE(T, D)                                                  \
-  template __global__ void bwd_pre_kernel<T, D, true>(                            \
+#define FA_BWD_INSTANTIATE_DP(T, D, RAW)                                              \
+  template __global__ void bwd_pre_kernel<T, D, true, RAW>(                         \
       const uint16_t*, const uint16_t*, const float*, const uint16_t*, const uint16_t*, \
       const uint16_t*, float*, float*, uint32_t*, int, int, int, int, Layout);      \
-  template __global__ void bwd_dkdv_kernel<T, D, true, false, false>(BwdParams);   \
-  template __global__ void bwd_dkdv_kernel<T, D, false, false, false>(BwdParams);  \
-  template __global__ void bwd_dkdv_kernel<T, D, false, true, false>(BwdParams);   \
-  template __global__ void bwd_dkdv_kernel<T, D, true, false, true>(BwdParams);    \
-  template __global__ void bwd_dkdv_kernel<T, D, false, false, true>(BwdParams);   \
-  template __global__ void bwd_dq_kernel<T, D, true, false, false>(BwdParams);     \
-  template __global__ void bwd_dq_kernel<T, D, false, false, false>(BwdParams);    \
-  template __global__ void bwd_dq_kernel<T, D, true, false, true>(BwdParams);      \
-  template __global__ void bwd_dq_kernel<T, D, false, false, true>(BwdParams);     \
-  template __global__ void bwd_dq_kernel<T, D, false, true, false>(BwdParams);     \
-  template __global__ void bwd_fused_kernel<T, D, true, false, false>(BwdParams);  \
-  template __global__ void bwd_fused_kernel<T, D, false, false, false>(BwdParams); \
-  template __global__ void bwd_fused_kernel<T, D, true, false, true>(BwdParams);   \
-  template __global__ void bwd_fused_kernel<T, D, false, false, true>(BwdParams);  \
-  template __global__ void bwd_fused_kernel<T, D, false, true, false>(BwdParams);  \
-  template __global__ void bwd_prep_head_kernel<T, D>(                             \
+  template __global__ void bwd_prep_head_kernel<T, D, RAW>(                         \
       const uint16_t*, const uint16_t*, const float*, const uint16_t*, const uint16_t*, \
       const uint16_t*, float*, float*, uint32_t*, float, uint16_t*, uint16_t*, uint16_t*, \
       float*, float*, int, int, int, int, Layout);                                 \
-  template __global__ void bwd_convert_kernel<T, D>(                               \
+  template __global__ void bwd_convert_kernel<T, D, RAW>(                           \
       const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*,   \
       const uint32_t*, int, uint32_t*, float,                                        \
       uint16_t*, uint16_t*, uint16_t*, float*, float*, int, int, int, int, int, int, Layout);
+#define FA_BWD_INSTANTIATE_GR(T, D, RAW)                                              \
+  template __global__ void bwd_dkdv_kernel<T, D, true, false, false, RAW>(BwdParams);   \
+  template __global__ void bwd_dkdv_kernel<T, D, false, false, false, RAW>(BwdParams);  \
+  template __global__ void bwd_dkdv_kernel<T, D, false, true, false, RAW>(BwdParams);   \
+  template __global__ void bwd_dkdv_kernel<T, D, true, false, true, RAW>(BwdParams);    \
+  template __global__ void bwd_dkdv_kernel<T, D, false, false, true, RAW>(BwdParams);   \
+  template __global__ void bwd_dq_kernel<T, D, true, false, false, RAW>(BwdParams);     \
+  template __global__ void bwd_dq_kernel<T, D, false, false, false, RAW>(BwdParams);    \
+  template __global__ void bwd_dq_kernel<T, D, true, false, true, RAW>(BwdParams);      \
+  template __global__ void bwd_dq_kernel<T, D, false, false, true, RAW>(BwdParams);     \
+  template __global__ void bwd_dq_kernel<T, D, false, true, false, RAW>(BwdParams);     \
+  template __global__ void bwd_fused_kernel<T, D, true, false, false, RAW>(BwdParams);  \
+  template __global__ void bwd_fused_kernel<T, D, false, false, false, RAW>(BwdParams); \
+  template __global__ void bwd_fused_kernel<T, D, true, false, true, RAW>(BwdParams);   \
+  template __global__ void bwd_fused_kernel<T, D, false, false, true, RAW>(BwdParams);  \
+  template __global__ void bwd_fused_kernel<T, D, false, true, false, RAW>(BwdParams);
+#define FA_BWD_INSTANTIATE(T, D)                                                  \
+  FA_BWD_INSTANTIATE_DP(T, D, use_raw<T>())                                       \
+  FA_BWD_INSTANTIATE_GR(T, D, use_raw<T>())
 FA_BWD_INSTANTIATE(__bf16, 32)
 FA_BWD_INSTANTIATE(__bf16, 64)
 FA_BWD_INSTANTIATE(__bf16, 96)
@@ -1121,6 +1195,8 @@ FA_BWD_INSTANTIATE(_Float16, 64)
 FA_BWD_INSTANTIATE(_Float16, 96)
 FA_BWD_INSTANTIATE(_Float16, 128)
 #undef FA_BWD_INSTANTIATE
+#undef FA_BWD_INSTANTIATE_DP
+#undef FA_BWD_INSTANTIATE_GR
 
 // The D pass in one launch (one workgroup per head) when there are enough
 // heads to spread over the GPU and each is short; otherwise the two
@@ -1129,6 +1205,81 @@ FA_BWD_INSTANTIATE(_Float16, 128)
 // at 8 x 12 x 1024; 67 -> 63 us at 8 x 16 x 2048; 26 -> 25 us at 2 x 16 x 1024;
 // but 60 -> 94 us at 4 x 16 x 4096 (too few workgroups for the bytes).
 inline bool head_prep(int N, int BH) { return N <= kHeadPrepMaxN && BH >= 32; }
+
+// The gradient launches of stage 0 or 4 (one grid of dK/dV and dQ
+// workgroups), 2 (dK/dV) or 3 (dQ).
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool RAW>
+hipError_t launch_grads(BwdParams p, hipStream_t stream, int stage) {
+  p.ntiles = (p.N + kBKV - 1) / kBKV;  // = (N + kBR - 1) / kBR
+  if (stage == 0 || stage == 4)
+    hipLaunchKernelGGL((bwd_fused_kernel<T, D, CAUSAL, SPARSE, DROP, RAW>),
+                       dim3(2 * p.ntiles * p.BH), dim3(256), 0, stream, p);
+  else if (stage == 2)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, SPARSE, DROP, RAW>),
+                       dim3(p.ntiles * p.BH), dim3(256), 0, stream, p);
+  else if (stage == 3)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, SPARSE, DROP, RAW>), dim3(p.ntiles * p.BH),
+                       dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+
+// The D pass: D, shift, maxima, the fp16 copies and the row terms, in one
+// launch (one workgroup per head) or two (maxima per chunk of rows, then the
+// copies); the raw path copies dO only.
+template <typename T, int D, bool RAW>
+hipError_t launch_dpass(const BwdArgs& a, char* ws, const BwdWorkspace& w) {
+  const int BH = a.B * a.H;
+  float* Dbuf = reinterpret_cast<float*>(ws + w.D);
+  float* shift = reinterpret_cast<float*>(ws + w.shift);
+  float* nDs = reinterpret_cast<float*>(ws + w.nDs);
+  float* nsh = reinterpret_cast<float*>(ws + w.nsh);
+  const float c = a.scale * kLog2e;
+  uint32_t* maxes = reinterpret_cast<uint32_t*>(ws + w.maxes);
+  uint32_t* part = reinterpret_cast<uint32_t*>(ws + w.part);
+  uint16_t* q16 = reinterpret_cast<uint16_t*>(ws + w.q16);
+  uint16_t* do16 = reinterpret_cast<uint16_t*>(ws + w.do16);
+  uint16_t* k16 = reinterpret_cast<uint16_t*>(ws + w.k16);
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* dO = static_cast<const uint16_t*>(a.dO);
+  const int rexp = a.drop.on ? a.drop.rexp : 0;
+  if (head_prep(a.N, BH)) {
+    hipLaunchKernelGGL((bwd_prep_head_kernel<T, D, RAW>), dim3(BH), dim3(1024), 0, a.stream,
+                       static_cast<const uint16_t*>(a.o), dO, a.lse, q,
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), Dbuf,
+                       shift, maxes, c, q16, k16, do16, nDs, nsh, a.N, BH, rexp, a.H, a.lay);
+    return hipGetLastError();
+  }
+  // row groups per workgroup of the D pass: enough for a grid of about
+  // 2048 workgroups, and at least enough that a head has at most
+  // kPreChunks workgroups (one partial maximum each)
+  constexpr int rpb = 256 / pre_tpr<D>();  // rows per group
+  const int64_t groups = (a.N + rpb - 1) / rpb;
+  const int64_t by_head = (groups + kPreChunks - 1) / kPreChunks;
+  const int64_t by_grid = (groups * BH + 2047) / 2048;
+  int iters = (int)(by_head > by_grid ? by_head : by_grid);
+  iters = iters < 1 ? 1 : iters;
+  const int pre_rows = rpb * iters;  // rows per workgroup
+  const int nchunk = (a.N + pre_rows - 1) / pre_rows;
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D, true, RAW>), dim3(BH, nchunk), dim3(256), 0, a.stream,
+                     static_cast<const uint16_t*>(a.o), dO, a.lse, q,
+                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), Dbuf,
+                     shift, part, a.N, BH, iters, a.H, a.lay);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // convert: row blocks per workgroup so that the grid stays near 4096
+  // workgroups (each reduces the partial maxima once)
+  constexpr int crpb = 256 / (D / 8);  // rows per block
+  const int64_t cblocks = (a.N + crpb - 1) / crpb;
+  int citers = (int)((cblocks * BH) / 4096);
+  citers = citers < 1 ? 1 : (citers > 16 ? 16 : citers);
+  const int rbph = (int)((cblocks + citers - 1) / citers);  // convert workgroups per head
+  hipLaunchKernelGGL((bwd_convert_kernel<T, D, RAW>), dim3((unsigned)((int64_t)BH * rbph)),
+                     dim3(256), 0, a.stream, q, static_cast<const uint16_t*>(a.k), dO, Dbuf,
+                     shift, part, nchunk, maxes, c, q16, k16, do16, nDs, nsh, a.N, BH, rbph,
+                     citers, rexp, a.H, a.lay);
+  return hipGetLastError();
+}
 
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t run_bwd(const BwdArgs& a, int stage) {
@@ -1148,44 +1299,9 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   uint16_t* k16 = reinterpret_cast<uint16_t*>(ws + w.k16);
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   const uint16_t* dO = static_cast<const uint16_t*>(a.dO);
-  if ((stage == 0 || stage == 1) && head_prep(a.N, BH)) {
-    hipLaunchKernelGGL((bwd_prep_head_kernel<T, D>), dim3(BH), dim3(1024), 0, a.stream,
-                       static_cast<const uint16_t*>(a.o), dO, a.lse, q,
-                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), Dbuf,
-                       shift, maxes, c, q16, k16, do16, nDs, nsh, a.N, BH,
-                       a.drop.on ? a.drop.rexp : 0, a.H, a.lay);
-    e = hipGetLastError();
-    if (e != hipSuccess || stage == 1) return e;
-  } else if (stage == 0 || stage == 1) {
-    // row groups per workgroup of the D pass: enough for a grid of about
-    // 2048 workgroups, and at least enough that a head has at most
-    // kPreChunks workgroups (one partial maximum each)
-    constexpr int rpb = 256 / pre_tpr<D>();  // rows per group
-    const int64_t groups = (a.N + rpb - 1) / rpb;
-    const int64_t by_head = (groups + kPreChunks - 1) / kPreChunks;
-    const int64_t by_grid = (groups * BH + 2047) / 2048;
-    int iters = (int)(by_head > by_grid ? by_head : by_grid);
-    iters = iters < 1 ? 1 : iters;
-    const int pre_rows = rpb * iters;  // rows per workgroup
-    const int nchunk = (a.N + pre_rows - 1) / pre_rows;
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D, true>), dim3(BH, nchunk), dim3(256), 0, a.stream,
-                       static_cast<const uint16_t*>(a.o), dO, a.lse, q,
-                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), Dbuf,
-                       shift, part, a.N, BH, iters, a.H, a.lay);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // convert: row blocks per workgroup so that the grid stays near 4096
-    // workgroups (each reduces the partial maxima once)
-    constexpr int crpb = 256 / (D / 8);  // rows per block
-    const int64_t cblocks = (a.N + crpb - 1) / crpb;
-    int citers = (int)((cblocks * BH) / 4096);
-    citers = citers < 1 ? 1 : (citers > 16 ? 16 : citers);
-    const int rbph = (int)((cblocks + citers - 1) / citers);  // convert workgroups per head
-    hipLaunchKernelGGL((bwd_convert_kernel<T, D>), dim3((unsigned)((int64_t)BH * rbph)),
-                       dim3(256), 0, a.stream, q, static_cast<const uint16_t*>(a.k), dO, Dbuf,
-                       shift, part, nchunk, maxes, c, q16, k16, do16, nDs, nsh, a.N, BH, rbph,
-                       citers, a.drop.on ? a.drop.rexp : 0, a.H, a.lay);
-    e = hipGetLastError();
+  constexpr bool raw = use_raw<T>();
+  if (stage == 0 || stage == 1) {
+    e = launch_dpass<T, D, raw>(a, ws, w);
     if (e != hipSuccess || stage == 1) return e;
   }
 
@@ -1215,6 +1331,7 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   p.nblk = (a.N + 127) / 128;
   p.period = (FA_BWD_SNAKE && CAUSAL) ? snake_period(p.BH) : 0;
   p.drop = a.drop;
+  p.sq = a.lay.q;
   p.sk = a.lay.k;
   p.sv = a.lay.v;
   p.sdO = a.lay.dO;
@@ -1222,26 +1339,7 @@ hipError_t run_bwd(const BwdArgs& a, int stage) {
   p.sdk = a.lay.dk;
   p.sdv = a.lay.dv;
 
-  if (stage == 0 || stage == 4) {
-    p.ntiles = (a.N + kBKV - 1) / kBKV;
-    hipLaunchKernelGGL((bwd_fused_kernel<T, D, CAUSAL, SPARSE, DROP>),
-                       dim3(2 * p.ntiles * p.BH), dim3(256), 0, a.stream, p);
-    return hipGetLastError();
-  }
-  if (stage == 2) {
-    p.ntiles = (a.N + kBKV - 1) / kBKV;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(p.ntiles * p.BH),
-                       dim3(256), 0, a.stream, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (stage == 3) {
-    p.ntiles = (a.N + kBR - 1) / kBR;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(p.ntiles * p.BH),
-                       dim3(256), 0, a.stream, p);
-    e = hipGetLastError();
-  }
-  return e;
+  return launch_grads<T, D, CAUSAL, SPARSE, DROP, raw>(p, a.stream, stage);
 }
 
 template <typename T, int D>
