@@ -148,11 +148,6 @@ __device__ __forceinline__ Scales bwd_scales_of(uint32_t mxq, uint32_t mxk, uint
   return s;
 }
 
-// the same from the maxima stored per (b, h) in maxes[4][BH]
-template <int D>
-__device__ __forceinline__ Scales bwd_scales(const uint32_t* maxes, int BH, int bh, float c) {
-  return bwd_scales_of<D>(maxes[bh], maxes[BH + bh], maxes[2 * BH + bh], maxes[3 * BH + bh], c);
-}
 
 // The raw path's scales: Q and K enter the products unscaled (in the
 // input type, exactly), so c multiplies the score accumulator in fp32
@@ -167,9 +162,6 @@ __device__ __forceinline__ Scales raw_scales_of(uint32_t mxv, uint32_t mxo, floa
   s.mul = true;
   s.m = c;
   return s;
-}
-__device__ __forceinline__ Scales bwd_raw_scales(const uint32_t* maxes, int BH, int bh, float c) {
-  return raw_scales_of(maxes[2 * BH + bh], maxes[3 * BH + bh], c);
 }
 
 // largest |x| of the 8 16-bit values in a 16-byte chunk, as float bits
@@ -616,20 +608,46 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
   const float* nD = p.nDs + (size_t)bh * N;
   const int L = valid_keys(p.key_len, b, N);
   const int k0 = kt * kBKV, kw = k0 + wave * 32, key = kw + l32;
-  const Scales sc =
-      RAW ? bwd_raw_scales(p.maxes, p.BH, bh, p.c) : bwd_scales<D>(p.maxes, p.BH, bh, p.c);
-  const int ek = sc.ek, ev = sc.ev;
+  // The prologue issues every load (the head's maxima, the first query
+  // tile's copies, this wave's keys and values) before it uses any, so that
+  // their global latencies overlap instead of adding up.
+  const uint32_t mxq = RAW ? 0u : p.maxes[bh], mxk = RAW ? 0u : p.maxes[p.BH + bh];
+  const uint32_t mxv = p.maxes[2 * p.BH + bh], mxo = p.maxes[3 * p.BH + bh];
+
+  const TileCopy<D, kBQ, NW> copy(wave, lane, qrs);  // Q; dO's tiles adjust to its stride
+  // copies of the query tile at row r0 (Q, dO and the two row terms)
+  auto load = [&](int r0, uint16_t* dq_, uint16_t* do_, float* dl, float* dd)
+      __attribute__((always_inline)) {
+    copy(Q, r0, N, dq_);
+    copy.copy_rs(dO, D, r0, N, do_);
+    if (wave == 0) copy_row_stat(nsh, r0, N, dl, lane);
+    if (wave == 1) copy_row_stat(nD, r0, N, dd, lane);
+  };
+  // Dense masks: the query tiles t0 .. nqt-1 (causal: the queries before k0
+  // see none of these keys); the first one's copies go out here.
+  const int nqt = (N + kBQ - 1) / kBQ;
+  const int t0 = CAUSAL ? k0 / kBQ : 0;
+  const bool primed = !SPARSE && k0 < L && nqt > t0;
+  if (primed) load(t0 * kBQ, sQ0, sO0, sL0, sD0);
 
   // this wave's keys (K, or K 2^-ek in fp16) and values (V 2^-ev, fp16) as
   // B operands (lane = key, k = d values)
-  qvec8 kf[KS];
-  vec8 vf[KS];
+  u32x4 kraw[KS], vraw[KS];
   const uint16_t* const Kin = p.k + b * p.sk.b + hd * p.sk.h;
   const uint16_t* const Vin = p.v + b * p.sv.b + hd * p.sv.h;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    u32x4 kr = ldg16_row(Kin, key, p.sk.n, ks * 16 + h * 8, N);
-    u32x4 vr = ldg16_row(Vin, key, p.sv.n, ks * 16 + h * 8, N);
+    kraw[ks] = ldg16_row(Kin, key, p.sk.n, ks * 16 + h * 8, N);
+    vraw[ks] = ldg16_row(Vin, key, p.sv.n, ks * 16 + h * 8, N);
+  }
+  const Scales sc =
+      RAW ? raw_scales_of(mxv, mxo, p.c) : bwd_scales_of<D>(mxq, mxk, mxv, mxo, p.c);
+  const int ek = sc.ek, ev = sc.ev;
+  qvec8 kf[KS];
+  vec8 vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 kr = kraw[ks], vr = vraw[ks];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (!RAW)
@@ -657,7 +675,6 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
     for (int db = 0; db < DB; ++db)
       toff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec, db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
 
-  const TileCopy<D, kBQ, NW> copy(wave, lane, qrs);  // Q; dO's tiles adjust to its stride
   const bool any_key = kw < L;  // every key of this wave padded away -> zero gradients
 
   auto compute = [&](const uint16_t* tq, const uint16_t* to, const float* tl, const float* td,
@@ -785,17 +802,11 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
     }
   };
 
-  // query tiles t -> first row row0(t); copies one tile ahead, one barrier per tile
-  auto walk = [&](int ntiles, auto row0) __attribute__((always_inline)) {
+  // query tiles t -> first row row0(t); copies one tile ahead, one barrier
+  // per tile (`primed`: the first tile's copies are already in flight)
+  auto walk = [&](int ntiles, auto row0, bool primed_) __attribute__((always_inline)) {
     if (ntiles <= 0) return;
-    auto load = [&](int r0, uint16_t* dq_, uint16_t* do_, float* dl, float* dd)
-        __attribute__((always_inline)) {
-      copy(Q, r0, N, dq_);
-      copy.copy_rs(dO, D, r0, N, do_);
-      if (wave == 0) copy_row_stat(nsh, r0, N, dl, lane);
-      if (wave == 1) copy_row_stat(nD, r0, N, dd, lane);
-    };
-    load(row0(0), sQ0, sO0, sL0, sD0);
+    if (!primed_) load(row0(0), sQ0, sO0, sL0, sD0);
     auto step = [&](int t, const uint16_t* cq, const uint16_t* co, const float* cl,
                     const float* cd, uint16_t* nq, uint16_t* no, float* nl, float* nd)
         __attribute__((always_inline)) {
@@ -818,12 +829,10 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
         const int wend = w0 + kListMax < p.nblk ? w0 + kListMax : p.nblk;
         const int cnt = list_blocks(mcol, p.nblk, w0, wend, sList, wave, lane);
         __syncthreads();
-        walk(2 * cnt, [&](int t) { return sList[t >> 1] * 128 + (t & 1) * kBQ; });
+        walk(2 * cnt, [&](int t) { return sList[t >> 1] * 128 + (t & 1) * kBQ; }, false);
       }
     } else {
-      const int nqt = (N + kBQ - 1) / kBQ;
-      const int t0 = CAUSAL ? k0 / kBQ : 0;  // queries before k0 see none of these keys
-      walk(nqt - t0, [&](int t) { return (t0 + t) * kBQ; });
+      walk(nqt - t0, [&](int t) { return (t0 + t) * kBQ; }, primed);
     }
   }
 
@@ -899,21 +908,27 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
   const uint16_t* V = p.v + b * p.sv.b + hd * p.sv.h;
   const int L = valid_keys(p.key_len, b, N);
   const int q0 = qt * kBR, qw = q0 + wave * 32, query = qw + l32;
-  const Scales sc =
-      RAW ? bwd_raw_scales(p.maxes, p.BH, bh, p.c) : bwd_scales<D>(p.maxes, p.BH, bh, p.c);
-  // dS is rounded to fp16 (raw path: the input type) for dQ = dS K.  dP and D here are unscaled (raw
-  // dO against raw V), so P carries the power of two 2^kq, kq = -(eo + ev),
-  // that the dK/dV kernel's dS gets from its scaled dO and V copies: then
-  // |dS'| = |P 2^kq (dP - D)| <= 2 d max|dO'| max|V'| < 2^15 for d <= 128,
-  // whatever the magnitudes of dO and V, and entries of ordinary size stay
-  // clear of fp16's subnormal range.  kq enters the exponent through the
-  // row term (no instruction per score) and is undone exactly in the
-  // epilogue.  With dropout P also carries 2^-rexp, from the row term the
-  // convert pass wrote.
-  const int kq = -(sc.eo + sc.ev);
-  // D of this lane's query (dropout: subtracted after the mask)
-  const float dq_D = DROP ? ldg_f32(p.Dbuf + (size_t)bh * N, query, N, 0.f) : 0.f;
+  // The prologue issues every load (the head's maxima, the first key tile's
+  // copies, this wave's queries, output gradients and row terms) before it
+  // uses any, so that their global latencies overlap instead of adding up.
+  const uint32_t mxq = RAW ? 0u : p.maxes[bh], mxk = RAW ? 0u : p.maxes[p.BH + bh];
+  const uint32_t mxv = p.maxes[2 * p.BH + bh], mxo = p.maxes[3 * p.BH + bh];
 
+  // chunk offsets for K's tiles; V's tiles adjust them when its row stride
+  // differs
+  const TileCopy<D, kBC, NW> copy(wave, lane, krs);
+  // Dense masks: key tiles 0 .. nkt-1 (causal: up to the last query's
+  // diagonal); the first one's copies go out here.
+  int nkt = (L + kBC - 1) / kBC;
+  if (CAUSAL) {
+    const int last = (q0 + kBR < N ? q0 + kBR : N) - 1;
+    nkt = nkt < last / kBC + 1 ? nkt : last / kBC + 1;
+  }
+  const bool primed = !SPARSE && nkt > 0;
+  if (primed) {
+    copy(K, 0, N, sK0);
+    copy.copy_rs(V, p.sv.n, 0, N, sV0);
+  }
   // this wave's queries (c Q 2^-eq, fp16) and output gradients as B
   // operands (lane = query, k = d values)
   hvec8 qf[KS];
@@ -927,6 +942,22 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
                              : ldg16_row(p.q16 + base, query, D, ks * 16 + h * 8, N));
     of[ks] = as_vec8<T>(ldg16_row(dOin, query, p.sdO.n, ks * 16 + h * 8, N));
   }
+  // the row values of this lane's query: -shift 2^-f and D
+  const float nsh_q = ldg_f32(p.nsh + (size_t)bh * N, query, N, neg_inf());
+  const float D_q = ldg_f32(p.Dbuf + (size_t)bh * N, query, N, 0.f);
+  const float dq_D = DROP ? D_q : 0.f;  // dropout: D is subtracted after the mask
+  const Scales sc =
+      RAW ? raw_scales_of(mxv, mxo, p.c) : bwd_scales_of<D>(mxq, mxk, mxv, mxo, p.c);
+  // dS is rounded to fp16 (raw path: the input type) for dQ = dS K.  dP and D here are unscaled (raw
+  // dO against raw V), so P carries the power of two 2^kq, kq = -(eo + ev),
+  // that the dK/dV kernel's dS gets from its scaled dO and V copies: then
+  // |dS'| = |P 2^kq (dP - D)| <= 2 d max|dO'| max|V'| < 2^15 for d <= 128,
+  // whatever the magnitudes of dO and V, and entries of ordinary size stay
+  // clear of fp16's subnormal range.  kq enters the exponent through the
+  // row term (no instruction per score) and is undone exactly in the
+  // epilogue.  With dropout P also carries 2^-rexp, from the row term the
+  // convert pass wrote.
+  const int kq = -(sc.eo + sc.ev);
   // the row terms of this lane's query (-shift 2^-f for the scores, -D for
   // dP; dropout subtracts D after the mask instead), replicated: every
   // element of a lane's 32 x 32 accumulator block belongs to its query, so
@@ -937,8 +968,8 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
     // the exponent is m (nsh + S'') when the accumulator is rescaled by m
     // (m = 2^f, or c 2^f in exact mode), else nsh + S''
     const float kqm = sc.mul ? (float)kq / sc.m : (float)kq;
-    const float ns = ldg_f32(p.nsh + (size_t)bh * N, query, N, neg_inf()) + kqm;
-    const float nd = DROP ? 0.f : -ldg_f32(p.Dbuf + (size_t)bh * N, query, N, 0.f);
+    const float ns = nsh_q + kqm;
+    const float nd = DROP ? 0.f : -D_q;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       s_init[e] = ns;
@@ -960,10 +991,6 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
 #pragma unroll
     for (int db = 0; db < DB; ++db)
       toff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec, db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
-
-  // chunk offsets for K's tiles; V's tiles adjust them when its row stride
-  // differs
-  const TileCopy<D, kBC, NW> copy(wave, lane, krs);
 
   // `prefetch` starts the copies of the next tile; it runs inside the
   // compute, after the score products are issued, so that the copies (which
@@ -1052,10 +1079,13 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
     }
   };
 
-  auto walk = [&](int ntiles, auto key0) __attribute__((always_inline)) {
+  // `primed`: the first tile's copies are already in flight
+  auto walk = [&](int ntiles, auto key0, bool primed_) __attribute__((always_inline)) {
     if (ntiles <= 0) return;
-    copy(K, key0(0), N, sK0);
-    copy.copy_rs(V, p.sv.n, key0(0), N, sV0);
+    if (!primed_) {
+      copy(K, key0(0), N, sK0);
+      copy.copy_rs(V, p.sv.n, key0(0), N, sV0);
+    }
     auto step = [&](int t, const uint16_t* ck, const uint16_t* cv, uint16_t* nk, uint16_t* nv)
         __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -1082,15 +1112,10 @@ __device__ __forceinline__ void bwd_dq_body(BwdParams p, int wg, DqLds<D, SPARSE
       const int wend = w0 + kListMax < p.nblk ? w0 + kListMax : p.nblk;
       const int cnt = list_blocks(mrow, 1, w0, wend, sList, wave, lane);
       __syncthreads();
-      walk(2 * cnt, [&](int t) { return sList[t >> 1] * 128 + (t & 1) * kBC; });
+      walk(2 * cnt, [&](int t) { return sList[t >> 1] * 128 + (t & 1) * kBC; }, false);
     }
   } else {
-    int nkt = (L + kBC - 1) / kBC;
-    if (CAUSAL) {
-      const int last = (q0 + kBR < N ? q0 + kBR : N) - 1;
-      nkt = nkt < last / kBC + 1 ? nkt : last / kBC + 1;
-    }
-    walk(nkt, [](int t) { return t * kBC; });
+    walk(nkt, [](int t) { return t * kBC; }, primed);
   }
 
   if (qok) {  // dQ = scale 2^(ek - kq + rexp) (dS' K')

@@ -132,6 +132,18 @@ __device__ __forceinline__ u32x4 ldg16_row(const uint16_t* base, int row, int64_
   return row < nrows ? v : z;
 }
 
+// The same without the zero: rows >= nrows read a copy of the last row.
+// For operands whose rows past the end reach only outputs that are never
+// stored (the queries of the forward), this leaves the load's destination
+// free of a select, so the compiler can issue a run of them back to back
+// even where registers are scarce (with the select it reuses one
+// destination and waits for each load in turn).
+__device__ __forceinline__ u32x4 ldg16_clamp(const uint16_t* base, int row, int64_t rs, int col,
+                                             int nrows) {
+  const int r = row < nrows ? row : nrows - 1;
+  return *reinterpret_cast<const u32x4*>(base + (int64_t)r * rs + col);
+}
+
 // element i of a float array of n >= 1 elements, `other` for i >= n (a
 // select after an unconditional load, as above)
 __device__ __forceinline__ float ldg_f32(const float* a, int i, int n, float other) {

@@ -105,258 +105,265 @@ __global__ __launch_bounds__(64 * NW, FA_FWD_WAVES_PER_SIMD) void fwd_kernel(Fwd
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   int rank, bh;
-  // Dense causal: a workgroup takes the query tiles nqt-1-r and r of one
-  // head in turn, so every workgroup sees the same number of key tiles and
-  // all of them end together; otherwise a workgroup takes one tile.
-  constexpr bool kPairs = CAUSAL && !SPARSE;
-  map_workgroup(blockIdx.x, kPairs ? (p.nqt + 1) / 2 : p.nqt, p.BH, p.period, &rank, &bh);
-  const int npass = kPairs && p.nqt - 1 - rank != rank ? 2 : 1;
-  for (int pass = 0; pass < npass; ++pass) {
-    const int qt = CAUSAL ? (pass == 0 ? p.nqt - 1 - rank : rank) : rank;
-    const int b = bh / p.H, hd = bh - b * p.H, N = p.N;
-    const uint16_t* Q = p.q + b * p.sq.b + hd * p.sq.h;
-    const uint16_t* K = p.k + b * p.sk.b + hd * p.sk.h;
-    const uint16_t* V = p.v + b * p.sv.b + hd * p.sv.h;
-    const int L = valid_keys(p.key_len, b, N);
-    const int q0 = qt * BR, qw = q0 + wave * QW;
-    const float c = p.c;
+  // One query tile per workgroup; causal grids take the longest tiles (the
+  // most keys) first, so that the dispatcher fills the compute units that
+  // finish early with the short tiles at the end.
+  map_workgroup(blockIdx.x, p.nqt, p.BH, p.period, &rank, &bh);
+  const int qt = CAUSAL ? p.nqt - 1 - rank : rank;
+  const int b = bh / p.H, hd = bh - b * p.H, N = p.N;
+  const uint16_t* Q = p.q + b * p.sq.b + hd * p.sq.h;
+  const uint16_t* K = p.k + b * p.sk.b + hd * p.sk.h;
+  const uint16_t* V = p.v + b * p.sv.b + hd * p.sv.h;
+  const int L = valid_keys(p.key_len, b, N);
+  const int q0 = qt * BR, qw = q0 + wave * QW;
+  const float c = p.c;
 
-    // This wave's queries as B operands of S^T = K Q^T: lane = query column
-    // l32 of block qb, k = d values 16 ks + 8 h .. +7.
-    vec8 qf[NQB][KS];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int row = qw + qb * 32 + l32;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qf[qb][ks] = as_vec8<T>(ldg16_row(Q, row, p.sq.n, ks * 16 + h * 8, N));
-    }
+  // one set of chunk offsets for K's row stride; V (normally the same
+  // stride) adjusts them when its stride differs
+  const TileCopy<D, kBC, NW> copy(wave, lane, p.sk.n);
+  // Dense masks: key tiles 0 .. nkt-1 (causal: up to the diagonal of the
+  // last query).  The first tile's copies are issued before the loads of
+  // this wave's queries below, so that the two global latencies overlap.
+  int nkt = (L + kBC - 1) / kBC;
+  if (CAUSAL) {
+    const int last = (q0 + BR < N ? q0 + BR : N) - 1;
+    nkt = nkt < last / kBC + 1 ? nkt : last / kBC + 1;
+  }
+  const bool primed = !SPARSE && nkt > 0;
+  if (primed) {
+    copy(K, 0, N, sK0);
+    copy.copy_rs(V, p.sv.n, 0, N, sV0);
+  }
 
-    float m[NQB], mc[NQB], l[NQB];  // reference max (raw score), m * c, partial row sum
-    f32x16 acc[DB][NQB];            // O^T, relative to the reference
+  // This wave's queries as B operands of S^T = K Q^T: lane = query column
+  // l32 of block qb, k = d values 16 ks + 8 h .. +7.
+  vec8 qf[NQB][KS];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      m[qb] = neg_inf();
-      mc[qb] = neg_inf();  // "no reference yet": forces the rescaling path
-      l[qb] = 0.f;
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int row = qw + qb * 32 + l32;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[db][qb][e] = 0.f;
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      qf[qb][ks] = as_vec8<T>(ldg16_clamp(Q, row, p.sq.n, ks * 16 + h * 8, N));
+  }
 
-    // per-lane LDS element offsets (tile-invariant)
-    // K reads: row kb*32 + l32, chunk 2 ks + h  -> kb adds 32*D
-    int koff[KS];
+  float m[NQB], mc[NQB], l[NQB];  // reference max (raw score), m * c, partial row sum
+  f32x16 acc[DB][NQB];            // O^T, relative to the reference
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) koff[ks] = tile_off<D>(l32, ks * 16 + h * 8);
-    // V^T transpose reads: 16-lane group g4 = lane / 16; lanes of a group
-    // address rows 16a + 4h + sub/4 (+8 for the second read), columns
-    // db*32 + 16*(g4&1) + 4*(sub%4) .. +3.  a adds 16*D.
-    const int sub = lane & 15, g4 = lane >> 4;
-    int voff[2][DB];
+  for (int qb = 0; qb < NQB; ++qb) {
+    m[qb] = neg_inf();
+    mc[qb] = neg_inf();  // "no reference yet": forces the rescaling path
+    l[qb] = 0.f;
 #pragma unroll
-    for (int sec = 0; sec < 2; ++sec)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        voff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec,
-                                    db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
+      for (int e = 0; e < 16; ++e) acc[db][qb][e] = 0.f;
+  }
 
-    // one 64-key tile from LDS buffer `buf` (key rows kt0 ..)
-    auto compute = [&](const uint16_t* kt, const uint16_t* vt, int kt0) {
-      if (qw >= N) return;                        // wave has no query rows
-      if (CAUSAL && kt0 > qw + QW - 1) return;    // tile above the diagonal
+  // per-lane LDS element offsets (tile-invariant)
+  // K reads: row kb*32 + l32, chunk 2 ks + h  -> kb adds 32*D
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = tile_off<D>(l32, ks * 16 + h * 8);
+  // V^T transpose reads: 16-lane group g4 = lane / 16; lanes of a group
+  // address rows 16a + 4h + sub/4 (+8 for the second read), columns
+  // db*32 + 16*(g4&1) + 4*(sub%4) .. +3.  a adds 16*D.
+  const int sub = lane & 15, g4 = lane >> 4;
+  int voff[2][DB];
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      voff[sec][db] = tile_off<D>(4 * h + (sub >> 2) + 8 * sec,
+                                  db * 32 + 16 * (g4 & 1) + 4 * (sub & 3));
 
-      // S^T for 64 keys (2 blocks of 32) x QW queries
-      f32x16 s[2][NQB];
+  // one 64-key tile from LDS buffer `buf` (key rows kt0 ..)
+  auto compute = [&](const uint16_t* kt, const uint16_t* vt, int kt0) {
+    if (qw >= N) return;                        // wave has no query rows
+    if (CAUSAL && kt0 > qw + QW - 1) return;    // tile above the diagonal
+
+    // S^T for 64 keys (2 blocks of 32) x QW queries
+    f32x16 s[2][NQB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][qb][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const vec8 a = as_vec8<T>(lds16(kt + koff[ks] + kb * 32 * D));
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = Elt<T>::mfma32(a, qf[qb][ks], s[kb][qb]);
+      }
+
+    // -inf on keys past key_len / above the diagonal (boundary tiles only);
+    // accumulator element 4i+j of block kb is key kt0 + 32kb + 8i + 4h + j
+    const bool need_mask = (kt0 + kBC > L) || (CAUSAL && kt0 + kBC - 1 > qw);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) s[kb][qb][e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const vec8 a = as_vec8<T>(lds16(kt + koff[ks] + kb * 32 * D));
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = Elt<T>::mfma32(a, qf[qb][ks], s[kb][qb]);
-        }
+          for (int e = 0; e < 16; ++e) {
+            const int key = kt0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+            const int query = qw + qb * 32 + l32;
+            if (key >= L || (CAUSAL && key > query)) s[kb][qb][e] = neg_inf();
+          }
+    }
 
-      // -inf on keys past key_len / above the diagonal (boundary tiles only);
-      // accumulator element 4i+j of block kb is key kt0 + 32kb + 8i + 4h + j
-      const bool need_mask = (kt0 + kBC > L) || (CAUSAL && kt0 + kBC - 1 > qw);
-      if (need_mask) {
+    // P = exp2(c s - m c), packed to 16 bits; rs = this lane's part of the
+    // tile's row sum (of the rounded values)
+    uint32_t pk[2][NQB][8];
+    float rs[NQB];
+    auto exp_pack = [&](int qb, float msc) {
+      float r[4] = {0.f, 0.f, 0.f, 0.f};  // four independent sum chains
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};  // dropout draws of the current 8 keys
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float x0 = fast_exp2(fmaf(s[kb][qb][2 * e], c, -msc));
+          float x1 = fast_exp2(fmaf(s[kb][qb][2 * e + 1], c, -msc));
+          if constexpr (DROP) {
+            // elements 8c .. 8c+7 (pairs e = 4c .. 4c+3) are keys
+            // kt0 + 32 kb + 16 c + 4 h + {0..3, 8..11}: one generator call;
+            // pair e takes word e % 4, low half for x0 and high for x1
+            if ((e & 3) == 0)
+              philox4x32_10((uint32_t)drop_call(kt0 + kb * 32 + 16 * (e >> 2) + 4 * h),
+                            (uint32_t)(qw + qb * 32 + l32), (uint32_t)bh, p.drop.offset,
+                            p.drop.k0, p.drop.k1, w);
+            r[(2 * e) & 3] += x0;
+            r[(2 * e + 1) & 3] += x1;
+            const uint32_t wd = w[e & 3];
+            x0 = (wd & 0xFFFFu) >= p.drop.thresh ? x0 * p.drop.rinv : 0.f;
+            x1 = wd >= (p.drop.thresh << 16) ? x1 * p.drop.rinv : 0.f;
+            pk[kb][qb][e] = Elt<T>::pack2(x0, x1);
+          } else {
+            pk[kb][qb][e] = Elt<T>::pack2(x0, x1);
+            r[e & 3] = Elt<T>::sum2(pk[kb][qb][e], r[e & 3]);
+          }
+        }
+      }
+      rs[qb] = (r[0] + r[1]) + (r[2] + r[3]);
+    };
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      exp_pack(qb, mc[qb]);
+      over |= !(rs[qb] <= kRescaleAt);
+    }
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      // move the reference to the running maximum and rescale
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float mx = s[0][qb][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb)
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m[qb], mx);
+        const float msc = mn == neg_inf() ? 0.f : mn * c;
+        const float alpha = fast_exp2(m[qb] * c - msc);  // 0 while m = -inf
+        m[qb] = mn;
+        mc[qb] = mn == neg_inf() ? neg_inf() : msc;
+        l[qb] *= alpha;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int key = kt0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-              const int query = qw + qb * 32 + l32;
-              if (key >= L || (CAUSAL && key > query)) s[kb][qb][e] = neg_inf();
-            }
+        for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
+        exp_pack(qb, msc);
       }
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) l[qb] += rs[qb];
 
-      // P = exp2(c s - m c), packed to 16 bits; rs = this lane's part of the
-      // tile's row sum (of the rounded values)
-      uint32_t pk[2][NQB][8];
-      float rs[NQB];
-      auto exp_pack = [&](int qb, float msc) {
-        float r[4] = {0.f, 0.f, 0.f, 0.f};  // four independent sum chains
+    // O^T += V^T P^T, 16 keys per MFMA k-step (a = 16-key chunk of the tile)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};  // dropout draws of the current 8 keys
+    for (int a = 0; a < 4; ++a) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float x0 = fast_exp2(fmaf(s[kb][qb][2 * e], c, -msc));
-            float x1 = fast_exp2(fmaf(s[kb][qb][2 * e + 1], c, -msc));
-            if constexpr (DROP) {
-              // elements 8c .. 8c+7 (pairs e = 4c .. 4c+3) are keys
-              // kt0 + 32 kb + 16 c + 4 h + {0..3, 8..11}: one generator call;
-              // pair e takes word e % 4, low half for x0 and high for x1
-              if ((e & 3) == 0)
-                philox4x32_10((uint32_t)drop_call(kt0 + kb * 32 + 16 * (e >> 2) + 4 * h),
-                              (uint32_t)(qw + qb * 32 + l32), (uint32_t)bh, p.drop.offset,
-                              p.drop.k0, p.drop.k1, w);
-              r[(2 * e) & 3] += x0;
-              r[(2 * e + 1) & 3] += x1;
-              const uint32_t wd = w[e & 3];
-              x0 = (wd & 0xFFFFu) >= p.drop.thresh ? x0 * p.drop.rinv : 0.f;
-              x1 = wd >= (p.drop.thresh << 16) ? x1 * p.drop.rinv : 0.f;
-              pk[kb][qb][e] = Elt<T>::pack2(x0, x1);
-            } else {
-              pk[kb][qb][e] = Elt<T>::pack2(x0, x1);
-              r[e & 3] = Elt<T>::sum2(pk[kb][qb][e], r[e & 3]);
-            }
-          }
-        }
-        rs[qb] = (r[0] + r[1]) + (r[2] + r[3]);
-      };
-      bool over = false;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        exp_pack(qb, mc[qb]);
-        over |= !(rs[qb] <= kRescaleAt);
-      }
-      if (__builtin_amdgcn_ballot_w64(over) != 0) {
-        // move the reference to the running maximum and rescale
+      for (int db = 0; db < DB; ++db) {
+        const vec8 va = join8<T>(lds_tr4(vt + voff[0][db] + a * 16 * D),
+                                 lds_tr4(vt + voff[1][db] + a * 16 * D));
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-          float mx = s[0][qb][0];
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float mn = fmaxf(m[qb], mx);
-          const float msc = mn == neg_inf() ? 0.f : mn * c;
-          const float alpha = fast_exp2(m[qb] * c - msc);  // 0 while m = -inf
-          m[qb] = mn;
-          mc[qb] = mn == neg_inf() ? neg_inf() : msc;
-          l[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
-          exp_pack(qb, msc);
+          const uint32_t* pp = &pk[a >> 1][qb][(a & 1) * 4];
+          const u32x4 pb = {pp[0], pp[1], pp[2], pp[3]};
+          acc[db][qb] = Elt<T>::mfma32(va, as_vec8<T>(pb), acc[db][qb]);
         }
       }
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) l[qb] += rs[qb];
+    }
+  };
 
-      // O^T += V^T P^T, 16 keys per MFMA k-step (a = 16-key chunk of the tile)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const vec8 va = join8<T>(lds_tr4(vt + voff[0][db] + a * 16 * D),
-                                   lds_tr4(vt + voff[1][db] + a * 16 * D));
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            const uint32_t* pp = &pk[a >> 1][qb][(a & 1) * 4];
-            const u32x4 pb = {pp[0], pp[1], pp[2], pp[3]};
-            acc[db][qb] = Elt<T>::mfma32(va, as_vec8<T>(pb), acc[db][qb]);
-          }
-        }
-      }
-    };
-
-    // one set of chunk offsets for K's row stride; V (normally the same
-    // stride) adjusts them when its stride differs
-    const TileCopy<D, kBC, NW> copy(wave, lane, p.sk.n);
-
-    // Walk `ntiles` tiles (first key of tile t = key0(t)) with the copy of
-    // tile t+1 in flight while tile t is computed.  One barrier per tile.
-    auto walk = [&](int ntiles, auto key0) {
-      if (ntiles <= 0) return;
+  // Walk `ntiles` tiles (first key of tile t = key0(t)) with the copy of
+  // tile t+1 in flight while tile t is computed.  One barrier per tile.
+  // `primed`: the first tile's copies are already in flight.
+  auto walk = [&](int ntiles, auto key0, bool primed_) {
+    if (ntiles <= 0) return;
+    if (!primed_) {
       copy(K, key0(0), N, sK0);
       copy.copy_rs(V, p.sv.n, key0(0), N, sV0);
-      auto step = [&](int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t landed
-        __syncthreads();                     // ... and every wave's; tile t-1 fully read
-        if (t + 1 < ntiles) {
-          const int nk = key0(t + 1);
-          copy(K, nk, N, kn);
-          copy.copy_rs(V, p.sv.n, nk, N, vn);
-        }
-        compute(kc, vc, key0(t));
-      };
-      for (int t = 0; t < ntiles; t += 2) {
-        step(t, sK0, sV0, sK1, sV1);
-        if (t + 1 < ntiles) step(t + 1, sK1, sV1, sK0, sV0);
+    }
+    auto step = [&](int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t landed
+      __syncthreads();                     // ... and every wave's; tile t-1 fully read
+      if (t + 1 < ntiles) {
+        const int nk = key0(t + 1);
+        copy(K, nk, N, kn);
+        copy.copy_rs(V, p.sv.n, nk, N, vn);
       }
-      __syncthreads();  // LDS free for the caller
+      compute(kc, vc, key0(t));
     };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, sK0, sV0, sK1, sV1);
+      if (t + 1 < ntiles) step(t + 1, sK1, sV1, sK0, sV0);
+    }
+    __syncthreads();  // LDS free for the caller
+  };
 
-    if (SPARSE) {
-      // Active 128-key blocks of this 128-query block row, two tiles each,
-      // gathered into LDS a window of kListMax blocks at a time.
-      const uint8_t* mrow = p.block_mask + (size_t)qt * p.nblk;
-      for (int w0 = 0; w0 < p.nblk; w0 += kListMax) {
-        const int wend = w0 + kListMax < p.nblk ? w0 + kListMax : p.nblk;
-        int cnt = 0;
-        for (int j0 = w0; j0 < wend; j0 += 64) {
-          const int jb = j0 + lane;
-          const bool on = jb < wend && mrow[jb] != 0;
-          const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
-          if (wave == 0 && on) sList[cnt + __builtin_popcountll(bal & ((1ull << lane) - 1))] = jb;
-          cnt += __builtin_popcountll(bal);
+  if (SPARSE) {
+    // Active 128-key blocks of this 128-query block row, two tiles each,
+    // gathered into LDS a window of kListMax blocks at a time.
+    const uint8_t* mrow = p.block_mask + (size_t)qt * p.nblk;
+    for (int w0 = 0; w0 < p.nblk; w0 += kListMax) {
+      const int wend = w0 + kListMax < p.nblk ? w0 + kListMax : p.nblk;
+      int cnt = 0;
+      for (int j0 = w0; j0 < wend; j0 += 64) {
+        const int jb = j0 + lane;
+        const bool on = jb < wend && mrow[jb] != 0;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
+        if (wave == 0 && on) sList[cnt + __builtin_popcountll(bal & ((1ull << lane) - 1))] = jb;
+        cnt += __builtin_popcountll(bal);
+      }
+      __syncthreads();
+      walk(2 * cnt, [&](int t) { return sList[t >> 1] * 128 + (t & 1) * kBC; }, false);
+    }
+  } else {
+    walk(nkt, [](int t) { return t * kBC; }, primed);
+  }
+
+  // epilogue: O = O^T / l, lse = (m c + log2 l) ln 2
+  uint16_t* O = p.o + b * p.so.b + hd * p.so.h;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    const int query = qw + qb * 32 + l32;
+    if (query < N) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 o4 = {acc[db][qb][4 * i] * inv, acc[db][qb][4 * i + 1] * inv,
+                            acc[db][qb][4 * i + 2] * inv, acc[db][qb][4 * i + 3] * inv};
+          *reinterpret_cast<u32x2*>(O + (int64_t)query * p.so.n + db * 32 + 8 * i + 4 * h) =
+              pack4<T>(o4);
         }
-        __syncthreads();
-        walk(2 * cnt, [&](int t) { return sList[t >> 1] * 128 + (t & 1) * kBC; });
-      }
-    } else {
-      int nkt = (L + kBC - 1) / kBC;
-      if (CAUSAL) {
-        const int last = (q0 + BR < N ? q0 + BR : N) - 1;
-        nkt = nkt < last / kBC + 1 ? nkt : last / kBC + 1;
-      }
-      walk(nkt, [](int t) { return t * kBC; });
+      if (h == 0)
+        p.lse[(size_t)bh * N + query] = lt > 0.f ? (mc[qb] + fast_log2(lt)) * kLn2 : neg_inf();
     }
-
-    // epilogue: O = O^T / l, lse = (m c + log2 l) ln 2
-    uint16_t* O = p.o + b * p.so.b + hd * p.so.h;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const float lt = l[qb] + __shfl_xor(l[qb], 32);
-      const int query = qw + qb * 32 + l32;
-      if (query < N) {
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x4 o4 = {acc[db][qb][4 * i] * inv, acc[db][qb][4 * i + 1] * inv,
-                              acc[db][qb][4 * i + 2] * inv, acc[db][qb][4 * i + 3] * inv};
-            *reinterpret_cast<u32x2*>(O + (int64_t)query * p.so.n + db * 32 + 8 * i + 4 * h) =
-                pack4<T>(o4);
-          }
-        if (h == 0)
-          p.lse[(size_t)bh * N + query] = lt > 0.f ? (mc[qb] + fast_log2(lt)) * kLn2 : neg_inf();
-      }
-    }
-  }  // pass
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -557,7 +564,7 @@ hipError_t launch_fwd_kernel(const FwdArgs& a) {
   p.N = a.N;
   p.BH = a.B * a.H;
   p.nqt = (a.N + BR - 1) / BR;
-  p.period = 0;  // dense causal tiles are paired per workgroup; other tiles are uniform
+  p.period = 0;  // plain order: causal grids longest tile first
   p.c = a.scale * kLog2e;
   p.key_len = a.key_len;
   p.block_mask = a.block_mask;
@@ -567,9 +574,8 @@ hipError_t launch_fwd_kernel(const FwdArgs& a) {
   p.sk = a.lay.k;
   p.sv = a.lay.v;
   p.so = a.lay.o;
-  const int wgs_per_head = CAUSAL && !SPARSE ? (p.nqt + 1) / 2 : p.nqt;
   hipLaunchKernelGGL((fwd_kernel<T, D, NW, QW, CAUSAL, SPARSE, DROP>),
-                     dim3(wgs_per_head * p.BH), dim3(64 * NW), 0, a.stream, p);
+                     dim3(p.nqt * p.BH), dim3(64 * NW), 0, a.stream, p);
   return hipGetLastError();
 }
 
@@ -577,12 +583,13 @@ hipError_t launch_fwd_kernel(const FwdArgs& a) {
 // next to two query blocks) and for block-sparse masks (four waves share
 // each K/V tile of a 128-query mask row: measured 3-5 % faster than two
 // waves of 64 queries).  Dense 64-query waves at d <= 64 halve the LDS
-// reads per MFMA, but when their grid has fewer workgroups than the GPU has
-// compute units, workgroups of two 32-query waves (four times the
-// workgroups, each causal pair of equal work) finish sooner (causal B = 8,
-// H = 12, N = 1024: 192 -> 768 workgroups, 45.6 -> 33.8 us; four waves of
-// 32 queries, 384 workgroups: 37.0 us; with 256 workgroups on 256 CUs,
-// 64-query waves stay ahead).
+// reads per MFMA, but when their grid holds less work than one full tile per
+// compute unit (a causal grid counting half its tiles, the average causal
+// tile seeing half the keys), workgroups of two 32-query waves (four times
+// the workgroups) finish sooner (causal B = 8, H = 12, N = 1024: 768
+// instead of 192 workgroup-equivalents, 45.6 -> 33.8 us; four waves of 32
+// queries: 37.0 us; with 256 workgroup-equivalents on 256 CUs, 64-query
+// waves stay ahead).
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 hipError_t run_fwd(const FwdArgs& a) {
   constexpr int QW = (DROP || SPARSE) ? 32 : FwdShape<D>::QW;
