@@ -53,6 +53,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -70,14 +71,24 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 TRAFFIC_SOURCES = ("fa_api.cpp", "fa_bwd.hip", "fa_device.h", "fa_fwd.hip", "fa_internal.h")
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and blank-line or trailing-space
+    differences (string literals in these sources hold no comment marks)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    lines = (ln.rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_hash() -> str:
-    """Hash of the sources of the measured kernels; HBM-traffic figures are
-    only reported while those still match the build they were measured on."""
+    """Hash of the code (comments excluded) of the measured kernels'
+    sources; HBM-traffic figures are only reported while it still matches
+    the build they were measured on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "io_aware_tiled_05_amd", "csrc")
     for f in TRAFFIC_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

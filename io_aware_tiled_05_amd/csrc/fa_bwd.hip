@@ -53,6 +53,9 @@
 // (c max|Q| max|K| sqrt(d) > 64) leave c out of the Q copy, which rounding
 // c Q to fp16 would make inexact by ~2^-11 |c q.k| in the exponent, and
 // multiply the score accumulator by c 2^f in fp32 instead (see Scales).
+// fp16 inputs need no Q and K copies: their products are exact as given,
+// so those kernels use Q and K themselves in that exact mode, and the D
+// pass copies only dO (see use_raw).
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -866,7 +869,8 @@ __device__ __forceinline__ void bwd_dkdv_body(BwdParams p, int wg, DkdvLds<D, SP
 // dQ: one workgroup per 128 queries, 32 per wave
 //
 // Scores run on fp16 operands (c Q 2^-eq against K 2^-ek, the fp16 copies
-// of the convert pass) and dP on the input type.  The first k-step of each
+// of the convert pass; for fp16 inputs Q and K themselves) and dP on the
+// input type.  The first k-step of each
 // product starts from the query's -shift 2^-f (scores) or -D (dP) as its C
 // operand, so the accumulators end as the exponent of P and as dP - D: P is
 // one exponential and dS one multiply.
