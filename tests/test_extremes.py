@@ -3,7 +3,8 @@ oracle, same tolerances as the other parity tests).
 
 * q, k x 0.01: scores of about 1e-4, so the backward's per-head power-of-two
   scales cannot balance c Q and K to a zero net exponent and the kernels run
-  their rescaled-scores branch.
+  their rescaled-scores branch (bf16; fp16 inputs always use Q and K as
+  given, with c applied to the score accumulator).
 * q, k x 5: scores up to about 150 in base-2 units (the backward's
   exact-scores mode: c is not folded into the fp16 copy of Q); rows are
   nearly one-hot, exponentials of the first tile overflow against the
@@ -24,9 +25,8 @@ with nearly one-hot rows a dominant key collects that rounding from every
 row it dominates while its true gradient nearly cancels.  Measured: dK up to
 1.14 times the scaled gate at q, k x 5 (dQ 0.80, against 0.4 at x 1), so
 that case is held to 1.25 times it (the measured bound and a 10 % margin).
-The fp16 inputs, which run the same backward kernels after the same
-conversion but store O with 3 more bits, are held to the plain scaled gate
-there.  (Far beyond, at q, k x 30 with
+The fp16 inputs, whose O carries 3 more bits (and whose scores come from
+Q and K as given), are held to the plain scaled gate there.  (Far beyond, at q, k x 30 with
 logits near 3000, fp32 itself bounds the recomputed P to about 0.3 %; the
 exact-scores mode keeps dQ and dK within 0.7 % of their size there, against
 40 % without it.)
