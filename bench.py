@@ -453,8 +453,8 @@ def main():
         print(json.dumps(summarize_counters(fc, wc, cfc, cwc, int(mib) << 20, TRAFFIC_FILE)))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs the per-head kernels on a single "
-              "MI355X; --gpus above 1 is not supported", file=sys.stderr)
+        print("bench.py measures one GPU: the per-head kernels run on a single MI355X, and "
+              "--gpus above 1 is not supported", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

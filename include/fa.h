@@ -32,7 +32,7 @@
  * Errors.  Arguments are validated before any HIP call is made:
  *   FA_ERR_INVALID      a null pointer, a size out of range, a non-finite
  *                       or non-positive scale, a workspace that is too small;
- *   FA_ERR_UNSUPPORTED  a valid request this build does not implement
+ *   FA_ERR_UNSUPPORTED  a valid request the library does not implement
  *                       (d not in {32, 64, 96, 128}, block_size != 128, fp32
  *                       block-sparse);
  *   FA_ERR_HIP          a kernel launch failed (hipGetLastError).  Faults
